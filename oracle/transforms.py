@@ -1,0 +1,158 @@
+"""Per-block transforms: identity, Hadamard, WUS, WUSH (test infrastructure only).
+
+Source: "WUSH" news article (chain.bitekongjian.com), paragraph on the
+construction: the transform is assembled from a Cholesky factor of weight
+statistics (W), the U and S factors of an SVD, and a Hadamard matrix (H); it
+is non-orthogonal and block-diagonal, and it is built from second moments of
+weights and activations.  Paragraph on deployment: moments come from
+calibration data or an existing Hessian; Cholesky and SVD run per block, in
+parallel; at inference only the activations are transformed.  "WUSH:
+Near-Optimal Adaptive Transforms for LLM Quantization" (AI Radio episode),
+"Problem Setup and Goal": T_W and T_X are chosen to minimise the layer loss of
+q(T_W W)^T q(T_X X) against W^T X, so T_X = T_W^{-T} keeps the unquantized
+product unchanged.
+
+The pages name the factors but print no formula.  Reading used here (the
+plainest one consistent with every stated property; derivation in the design
+notes):
+
+    A_b = W_b W_b^T           (weights restricted to block b; not normalised)
+    B_b = X_b X_b^T / n       (activation second moment of block b)
+    A_b = W' W'^T             (Cholesky, W' lower triangular)
+    C_b = W'^T B_b W' = U diag(lam) U^T   (eigh; = K K^T with K = W'^T X_b/sqrt(n),
+                                           so U, S = sqrt(lam) are K's SVD factors)
+    T_W = H^ S^{+1/2} U^T W'^{-1}
+    T_X = H^ S^{-1/2} U^T W'^T            (= T_W^{-T})
+
+with H^ the orthonormal Sylvester Hadamard matrix (WUSH) or the identity (WUS).
+It minimises the first-order proxy  J(T) = tr(T A T^T) * tr(T^{-T} B T^{-1})
+(quantization noise proportional to signal energy, as the article's paragraph
+on FP optimality states), whose minimum is (sum sigma_i)^2.
+"""
+
+import numpy as np
+
+KINDS = ("identity", "hadamard", "wus", "wush")
+DAMPING = (0.0, 1e-10, 1e-8, 1e-6, 1e-4, 1e-2)
+SIGMA_FLOOR = 1e-12
+
+
+def hadamard(d):
+    """Sylvester Hadamard matrix, natural order: H[i, j] = (-1)**popcount(i & j)."""
+    i = np.arange(d)
+    bits = np.bitwise_and(i[:, None], i[None, :])
+    pop = np.zeros_like(bits)
+    for s in range(int(np.log2(d)) + 1):
+        pop += (bits >> s) & 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
+def hadamard_normalized(d):
+    """H / sqrt(d): orthogonal."""
+    return hadamard(d) / np.sqrt(d)
+
+
+def weight_moments(Wt, bs):
+    """A_b = W_b W_b^T in fp64 for every block.  Wt is [d_out][d_in] (nn.Linear)."""
+    Wt = np.asarray(Wt, dtype=np.float64)
+    d_out, d_in = Wt.shape
+    Wb = Wt.reshape(d_out, d_in // bs, bs)            # [o][b][i]
+    return np.einsum("obi,obj->bij", Wb, Wb)
+
+
+def activation_moments(Xt, bs):
+    """B_b = X_b X_b^T / n in fp64 for every block.  Xt is [n][d_in] (token-major)."""
+    Xt = np.asarray(Xt, dtype=np.float64)
+    n, d_in = Xt.shape
+    Xb = Xt.reshape(n, d_in // bs, bs)
+    return np.einsum("tbi,tbj->bij", Xb, Xb) / n
+
+
+def cholesky_damped(A):
+    """Lower Cholesky factor of A, retrying with A + eps*(tr A/bs)*I on failure.
+
+    Returns (L, eps_used).  Raises np.linalg.LinAlgError when every rung of the
+    damping ladder fails.
+    """
+    bs = A.shape[0]
+    t = np.trace(A) / bs
+    for eps in DAMPING:
+        try:
+            return np.linalg.cholesky(A + eps * t * np.eye(bs)), eps
+        except np.linalg.LinAlgError:
+            continue
+    raise np.linalg.LinAlgError("block moment not positive definite after damping")
+
+
+def eig_desc(C):
+    """Symmetric eigen-decomposition with eigenvalues in descending order.
+
+    Each eigenvector is signed so that its entry of largest magnitude is
+    positive (the lowest index wins a tie in magnitude).
+    """
+    lam, U = np.linalg.eigh(C)
+    order = np.argsort(-lam, kind="stable")
+    lam = lam[order]
+    U = U[:, order]
+    piv = np.argmax(np.abs(U), axis=0)                 # first max-|.| index per column
+    sgn = np.sign(U[piv, np.arange(U.shape[1])])
+    sgn[sgn == 0] = 1.0
+    return lam, U * sgn
+
+
+def block_factors(A, B):
+    """W', U, sigma for one block (fp64)."""
+    Wp, _ = cholesky_damped(A)
+    C = Wp.T @ B @ Wp
+    C = 0.5 * (C + C.T)
+    lam, U = eig_desc(C)
+    sig = np.sqrt(np.maximum(lam, 0.0))
+    sig = np.maximum(sig, SIGMA_FLOOR * sig[0]) if sig[0] > 0 else np.ones_like(sig)
+    return Wp, U, sig
+
+
+def block_transform(kind, A, B, bs=None):
+    """(T_X, T_W) for one block, fp64.  A / B may be None for identity / hadamard."""
+    bs = bs if bs is not None else A.shape[0]
+    if kind == "identity":
+        eye = np.eye(bs)
+        return eye, eye.copy()
+    if kind == "hadamard":
+        H = hadamard_normalized(bs)
+        return H, H.copy()
+    Wp, U, sig = block_factors(A, B)
+    left_x = np.diag(sig ** -0.5) @ U.T                # S^{-1/2} U^T
+    left_w = np.diag(sig ** 0.5) @ U.T                 # S^{+1/2} U^T
+    Tx = left_x @ Wp.T
+    Tw = left_w @ np.linalg.inv(Wp)
+    if kind == "wush":
+        H = hadamard_normalized(bs)
+        Tx = H @ Tx
+        Tw = H @ Tw
+    elif kind != "wus":
+        raise ValueError(kind)
+    return Tx, Tw
+
+
+def build_transforms(kind, Wt, Sx, bs):
+    """All blocks: returns (Tx, Tw) as float32 [nblk][bs][bs] and the fp64 versions.
+
+    Wt: [d_out][d_in] weights; Sx: [nblk][bs][bs] activation moments (may be
+    None for identity / hadamard).
+    """
+    d_in = np.asarray(Wt).shape[1]
+    nblk = d_in // bs
+    A = weight_moments(Wt, bs) if kind in ("wus", "wush") else None
+    Tx64 = np.empty((nblk, bs, bs))
+    Tw64 = np.empty((nblk, bs, bs))
+    for b in range(nblk):
+        Ab = A[b] if A is not None else None
+        Bb = np.asarray(Sx[b], dtype=np.float64) if Sx is not None else None
+        Tx64[b], Tw64[b] = block_transform(kind, Ab, Bb, bs)
+    return Tx64.astype(np.float32), Tw64.astype(np.float32), Tx64, Tw64
+
+
+def proxy_loss(T, A, B):
+    """First-order loss model J(T) = tr(T A T^T) * tr(T^{-T} B T^{-1})."""
+    Ti = np.linalg.inv(T)
+    return np.trace(T @ A @ T.T) * np.trace(Ti.T @ B @ Ti)
