@@ -1,0 +1,183 @@
+"""ctypes binding of libwush (argument marshalling only).
+
+Every function here has the name of the C entry point it wraps and only
+converts arguments (ints, floats, device pointers from torch tensors, the
+current HIP stream) and turns a non-OK status into an exception.  All
+computation happens inside libwush.so.  Importing this module fails loudly
+when the library has not been built: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+# torch ships its own HIP runtime.  Loading libwush.so first would map the
+# system HIP/HSA runtime as well, and two runtimes in one process do not see
+# each other's device state ("no ROCm-capable device" on launch, crashes in
+# later copies).  Importing torch first makes libwush bind to the runtime torch
+# already loaded (same soname).
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwush.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libwush.so not found at {LIB_PATH}; build it with "
+        "`python -m aware_block_transforms_amd.build` (no CPU fallback exists)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+# enums (must match include/wush.h)
+WUSH_OK, WUSH_E_ARG, WUSH_E_SHAPE, WUSH_E_NUMERIC, WUSH_E_HIP, WUSH_E_UNSUPPORTED = range(6)
+FORMATS = {"mxfp4": 0, "nvfp4": 1, "int4": 2}
+KINDS = {"identity": 0, "hadamard": 1, "wus": 2, "wush": 3}
+DTYPES = {"f32": 0, "bf16": 1}
+BLOCK = {"mxfp4": 32, "nvfp4": 16, "int4": 32}
+
+_i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_fp = ctypes.POINTER(ctypes.c_float)
+
+_SIGS = {
+    "wush_format_block": ([_i], _i),
+    "wush_block_moments": ([_i, _i, _i, _p, _p], _i),
+    "wush_build_transforms": ([_i, _i, _i, _i, _p, _p, _p, _p], _i),
+    "wush_transform_quant": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _p], _i),
+    "wush_nvfp4_global_scale": ([_i, _i, _i, _p, _p, _fp, _p], _i),
+    "wush_pack_weights": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
+    "wush_w4a4_gemm": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _f, _p, _p], _i),
+    "wush_layer_loss": ([_i, _i, _p, _p, _p, _p, _p], _i),
+    "wush_loss_ws_bytes": ([_i, _i], _sz),
+    "wush_had256_pack_weights": ([_i, _i, _p, _p, _p, _p], _i),
+    "wush_had256_gemv": ([_i, _i, _i, _p, _p, _p, _p, _p], _i),
+    "wush_had256_rotate": ([_i, _i, _p, _p, _p], _i),
+    "wush_status_string": ([_i], ctypes.c_char_p),
+    "wush_last_error": ([], ctypes.c_char_p),
+    "wush_version": ([], ctypes.c_char_p),
+}
+for _name, (_args, _ret) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _ret
+
+EXPORTED = tuple(_SIGS)
+
+
+class WushError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        detail = lib.wush_last_error().decode()
+        super().__init__(f"{where}: {lib.wush_status_string(status).decode()} ({status}): {detail}")
+
+
+def _check(status, where):
+    if status != WUSH_OK:
+        raise WushError(status, where)
+
+
+def _ptr(t):
+    """Raw address of a torch tensor / numpy array (or None)."""
+    if t is None:
+        return None
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _fmt(fmt):
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+# ----------------------------------------------------------------------------- host calls
+
+
+def wush_block_moments(bs, X, Sx):
+    """X: host float32 [n][d_in] (numpy or CPU tensor), Sx: host float32 [d_in/bs][bs][bs] out."""
+    n, d_in = X.shape
+    _check(lib.wush_block_moments(bs, n, d_in, _ptr(X), _ptr(Sx)), "wush_block_moments")
+
+
+def wush_build_transforms(kind, bs, W, Sx, Tx, Tw):
+    """Host arrays: W [d_out][d_in] f32, Sx [nblk][bs][bs] f32 (or None), Tx/Tw out."""
+    k = KINDS[kind] if isinstance(kind, str) else int(kind)
+    d_out, d_in = (W.shape if W is not None else (0, Tx.shape[0] * bs))
+    _check(lib.wush_build_transforms(k, bs, d_in, d_out, _ptr(W), _ptr(Sx), _ptr(Tx), _ptr(Tw)),
+           "wush_build_transforms")
+
+
+# ----------------------------------------------------------------------------- device calls
+
+
+def wush_transform_quant(fmt, X, Tx, codes, scales, g=0.0, stream=None):
+    """X: device [n][d_in] float32 or bfloat16; Tx: device [nblk][bs][bs] f32 or None (identity)."""
+    import torch
+    n, d_in = X.shape
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("X must be float32 or bfloat16")
+    _check(lib.wush_transform_quant(_fmt(fmt), xdt, n, d_in, _ptr(X), _ptr(Tx), float(g), _ptr(codes),
+                                    _ptr(scales), _stream(stream)), "wush_transform_quant")
+
+
+def wush_nvfp4_global_scale(X, Tx, stream=None):
+    import torch
+    n, d_in = X.shape
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    g = ctypes.c_float(0.0)
+    _check(lib.wush_nvfp4_global_scale(xdt, n, d_in, _ptr(X), _ptr(Tx), ctypes.byref(g), _stream(stream)),
+           "wush_nvfp4_global_scale")
+    return g.value
+
+
+def wush_pack_weights(fmt, W, Tw, codes, scales, stream=None):
+    """W: device [d_out][d_in] f32.  Returns the NVFP4 tensor scale (1.0 for other formats)."""
+    d_out, d_in = W.shape
+    g = ctypes.c_float(0.0)
+    _check(lib.wush_pack_weights(_fmt(fmt), d_out, d_in, _ptr(W), _ptr(Tw), _ptr(codes), _ptr(scales),
+                                 ctypes.byref(g), _stream(stream)), "wush_pack_weights")
+    return g.value
+
+
+def wush_w4a4_gemm(fmt, a_codes, a_scales, b_codes, b_scales, Y, a_g=1.0, b_g=1.0, stream=None):
+    M, N = Y.shape
+    K = a_codes.shape[1] * 2
+    _check(lib.wush_w4a4_gemm(_fmt(fmt), M, N, K, _ptr(a_codes), _ptr(a_scales), float(a_g), _ptr(b_codes),
+                              _ptr(b_scales), float(b_g), _ptr(Y), _stream(stream)), "wush_w4a4_gemm")
+
+
+def wush_loss_ws_bytes(M, N):
+    return lib.wush_loss_ws_bytes(M, N)
+
+
+def wush_layer_loss(Yhat, Yref, loss, ws, stream=None):
+    M, N = Yhat.shape
+    _check(lib.wush_layer_loss(M, N, _ptr(Yhat), _ptr(Yref), _ptr(loss), _ptr(ws), _stream(stream)),
+           "wush_layer_loss")
+
+
+def wush_had256_pack_weights(W, planes, scales, stream=None):
+    d_out, d_in = W.shape
+    _check(lib.wush_had256_pack_weights(d_out, d_in, _ptr(W), _ptr(planes), _ptr(scales), _stream(stream)),
+           "wush_had256_pack_weights")
+
+
+def wush_had256_gemv(x, planes, scales, y, stream=None):
+    batch, d_in = x.shape
+    d_out = y.shape[1]
+    _check(lib.wush_had256_gemv(batch, d_out, d_in, _ptr(x), _ptr(planes), _ptr(scales), _ptr(y),
+                                _stream(stream)), "wush_had256_gemv")
+
+
+def wush_had256_rotate(inp, out, stream=None):
+    rows, d_in = inp.shape
+    _check(lib.wush_had256_rotate(rows, d_in, _ptr(inp), _ptr(out), _stream(stream)), "wush_had256_rotate")
+
+
+def wush_version():
+    return lib.wush_version().decode()

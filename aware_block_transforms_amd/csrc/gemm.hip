@@ -1,0 +1,49 @@
+// wush_w4a4_gemm: argument checks and dispatch to the per-format kernels.
+//
+// "WUSH: Near-Optimal Adaptive Transforms for LLM Quantization" (AI Radio):
+// the W4A4 product of the transformed, quantized weights and activations; the
+// WUSH news article (experiments paragraph) evaluates it for MXFP4, NVFP4 and
+// INT4.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+
+namespace wush {
+wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
+                       float* Y, hipStream_t stream);
+wush_status gemm_nvfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, float ga, const uint8_t* B,
+                       const uint8_t* SB, float gb, float* Y, hipStream_t stream);
+wush_status gemm_int4(int M, int N, int K, const uint8_t* A, const uint16_t* SA, const uint8_t* B,
+                      const uint16_t* SB, float* Y, hipStream_t stream);
+}  // namespace wush
+
+extern "C" wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K, const uint8_t* a_codes,
+                                      const void* a_scales, float a_g, const uint8_t* b_codes, const void* b_scales,
+                                      float b_g, float* Y, void* stream) {
+  if (wush_format_block(fmt) == 0) return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: bad format %d", static_cast<int>(fmt));
+  if (M < 1 || N < 1 || K < 128 || K % 128)
+    return wush::fail(WUSH_E_SHAPE, "wush_w4a4_gemm: need M, N >= 1 and K a positive multiple of 128 (M=%d N=%d K=%d)",
+                      M, N, K);
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !Y) return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: null pointer");
+  if (!wush::aligned16(a_codes) || !wush::aligned16(b_codes) || !wush::aligned16(Y) ||
+      (reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(b_scales) & 3u))
+    return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: codes and Y must be 16-byte aligned, scales 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (fmt) {
+    case WUSH_MXFP4:
+      return wush::gemm_mxfp4(M, N, K, a_codes, static_cast<const uint8_t*>(a_scales), b_codes,
+                              static_cast<const uint8_t*>(b_scales), Y, s);
+    case WUSH_NVFP4:
+      if (!(a_g > 0.0f && a_g < 3.0e38f) || !(b_g > 0.0f && b_g < 3.0e38f))
+        return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: NVFP4 tensor scales must be positive and finite");
+      return wush::gemm_nvfp4(M, N, K, a_codes, static_cast<const uint8_t*>(a_scales), a_g, b_codes,
+                              static_cast<const uint8_t*>(b_scales), b_g, Y, s);
+    case WUSH_INT4:
+      return wush::gemm_int4(M, N, K, a_codes, static_cast<const uint16_t*>(a_scales), b_codes,
+                             static_cast<const uint16_t*>(b_scales), Y, s);
+  }
+  return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: bad format");
+}

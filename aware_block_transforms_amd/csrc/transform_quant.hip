@@ -1,0 +1,364 @@
+// Transform-then-quantize kernels for gfx950: the online activation step and
+// the offline weight packing of WUSH.
+//
+// WUSH news article (chain.bitekongjian.com), deployment paragraph: at
+// inference only the activations are transformed, one small matrix per block
+// of input channels; weights are transformed and quantized once, offline.
+// "WUSH: Near-Optimal Adaptive Transforms for LLM Quantization" (AI Radio),
+// "The gist": transform and quantizer run as one fused GPU kernel.
+//
+// Work mapping (CDNA4, wave64):
+//  * one wave owns one block b of channels and walks token tiles of 64; lane
+//    l holds token (tile*64 + l).  The block's bs x bs matrix is identical for
+//    every lane, so it is read with scalar loads into SGPRs and broadcast to
+//    the FMAs for free; the wave's x values stay in VGPRs.
+//  * y_i = fma chain over k (ascending, from +0) in fp32: bs*bs v_fma_f32 per
+//    lane and block.  All bs outputs of a block live in one lane, so the block
+//    maximum needs no cross-lane reduction.
+//  * the lane packs its bs codes into bs/2 contiguous bytes (one 16-byte store
+//    at bs = 32) and stores one scale.
+// The arithmetic is pinned (see wush.h): codes and scales are bit-exact
+// functions of (T, x).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kTileIters = 2;   // 64-token tiles per wave
+
+enum Fmt { kMX = 0, kNV = 1, kI4 = 2, kAmax = 3 };
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// E2M1 code: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, exact ties to the even
+// code, saturating, sign bit copied.  Counts the decision thresholds passed.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float m = fabsf(v);
+  uint32_t c = (m > 0.25f ? 1u : 0u) + (m >= 0.75f ? 1u : 0u) + (m > 1.25f ? 1u : 0u) +
+               (m >= 1.75f ? 1u : 0u) + (m > 2.5f ? 1u : 0u) + (m >= 3.5f ? 1u : 0u) +
+               (m > 5.0f ? 1u : 0u);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Same, but NaN encodes as 0 (needed where v may be 0 * inf).
+__device__ __forceinline__ uint32_t e2m1_code_nan0(float v) {
+  return (v == v) ? e2m1_code(v) : 0u;
+}
+
+// FP8 E4M3 (finite-only) of 0 <= s <= 448, round to nearest, ties to even.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (s < 0.015625f) {                       // below 2^-6: subnormal grid m * 2^-9
+    return static_cast<uint32_t>(rintf(s * 512.0f));   // 0..8 (8 = 2^-6, code 0x08)
+  }
+  uint32_t b = __float_as_uint(s);
+  b += 0x7ffffu + ((b >> 20) & 1u);          // round to 3 mantissa bits, ties to even
+  return (b >> 20) - (120u << 3);            // rebias exponent 127 -> 7
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t ex = (c >> 3) & 15u, m = c & 7u;
+  if (ex == 0) return static_cast<float>(m) * 0.001953125f;   // m * 2^-9
+  return __uint_as_float(((ex + 120u) << 23) | (m << 20));
+}
+
+template <int BS, bool BF16>
+__device__ __forceinline__ void load_block(const void* __restrict__ X, size_t off, float (&x)[BS]) {
+  if constexpr (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(X) + off);
+#pragma unroll
+    for (int q = 0; q < BS / 8; ++q) {
+      const uint4 w = p[q];
+      x[8 * q + 0] = bf16lo(w.x); x[8 * q + 1] = bf16hi(w.x);
+      x[8 * q + 2] = bf16lo(w.y); x[8 * q + 3] = bf16hi(w.y);
+      x[8 * q + 4] = bf16lo(w.z); x[8 * q + 5] = bf16hi(w.z);
+      x[8 * q + 6] = bf16lo(w.w); x[8 * q + 7] = bf16hi(w.w);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(X) + off);
+#pragma unroll
+    for (int q = 0; q < BS / 4; ++q) {
+      const float4 w = p[q];
+      x[4 * q + 0] = w.x; x[4 * q + 1] = w.y; x[4 * q + 2] = w.z; x[4 * q + 3] = w.w;
+    }
+  }
+}
+
+// y = T x with the pinned fp32 FMA chain.  Tb is wave-uniform.
+template <int BS>
+__device__ __forceinline__ void transform(const float* __restrict__ Tb, const float (&x)[BS], float (&y)[BS]) {
+#pragma unroll
+  for (int i = 0; i < BS; ++i) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < BS; ++k) acc = __builtin_fmaf(Tb[i * BS + k], x[k], acc);
+    y[i] = acc;
+  }
+}
+
+// Two E2M1 codes into byte `sel` of `old` (low nibble = a).  gfx950's packed FP4
+// conversion rounds to nearest with ties to the even code, saturates at 6 and keeps
+// the sign bit, which is exactly the pinned encoder for every non-NaN input; the
+// scale operand divides, so 1.0 leaves the values unchanged.
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t old, float a, float b, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 3);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void zero_words(uint32_t (&w)[N]) {
+#pragma unroll
+  for (int q = 0; q < N; ++q) w[q] = 0u;
+}
+
+template <int BS>
+__device__ __forceinline__ void store_codes(uint8_t* __restrict__ dst, const uint32_t (&w)[BS / 8]) {
+  if constexpr (BS == 32) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  }
+}
+
+// One kernel for the three formats plus an amax-only pass (NVFP4 tensor scale).
+template <int BS, int FMT, bool BF16, bool IDENT>
+__global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_kernel(
+    const void* __restrict__ X, const float* __restrict__ T, int n, int d_in, float g,
+    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nblk = d_in / BS;
+  const int blk = blockIdx.x * kWavesPerGroup + wave;
+  if (blk >= nblk) return;                       // wave-uniform
+  const float* __restrict__ Tb = IDENT ? nullptr : T + static_cast<size_t>(blk) * BS * BS;
+  const int tok_base = blockIdx.y * (kWave * kTileIters);
+  uint32_t run_max = 0;
+
+  // NVFP4 constants (uniform)
+  const float d6 = 6.0f * g;
+
+  float xn[BS];
+  int tok = tok_base + lane;
+  if (tok < n) load_block<BS, BF16>(X, static_cast<size_t>(tok) * d_in + static_cast<size_t>(blk) * BS, xn);
+
+#pragma unroll 1
+  for (int it = 0; it < kTileIters; ++it) {
+    float x[BS];
+#pragma unroll
+    for (int k = 0; k < BS; ++k) x[k] = xn[k];
+    const bool valid = tok < n;
+    const int tok_next = tok + kWave;
+    if (it + 1 < kTileIters && tok_next < n)
+      load_block<BS, BF16>(X, static_cast<size_t>(tok_next) * d_in + static_cast<size_t>(blk) * BS, xn);
+
+    float y[BS];
+    if constexpr (IDENT) {
+#pragma unroll
+      for (int k = 0; k < BS; ++k) y[k] = x[k];
+    } else {
+      transform<BS>(Tb, x, y);
+    }
+    uint32_t ab = 0;
+#pragma unroll
+    for (int k = 0; k < BS; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
+    const bool bad = ab >= 0x7f800000u;          // NaN or Inf in the block
+
+    if constexpr (FMT == kAmax) {
+      if (valid) run_max = max(run_max, ab);
+    } else if (valid) {
+      const size_t row = static_cast<size_t>(tok);
+      uint32_t w[BS / 8];
+#pragma unroll
+      for (int q = 0; q < BS / 8; ++q) w[q] = 0u;
+      if constexpr (FMT == kMX) {
+        const uint32_t ex = ab >> 23;
+        const uint32_t sbyte = ex > 2u ? ex - 2u : 0u;             // e + 127
+        const float inv = __uint_as_float((254u - sbyte) << 23);   // 2^-e
+#pragma unroll
+        for (int k = 0; k < BS / 2; ++k) w[k >> 2] = cvt_pair(w[k >> 2], y[2 * k] * inv, y[2 * k + 1] * inv, k & 3);
+        if (bad) zero_words(w);
+        reinterpret_cast<uint8_t*>(scales)[row * nblk + blk] = bad ? 0xffu : static_cast<uint8_t>(sbyte);
+      } else if constexpr (FMT == kNV) {
+        const float a = __uint_as_float(ab);
+        float s = fminf(a / d6, 448.0f);
+        const uint32_t s8 = bad ? 0u : e4m3_encode(s);
+        const float s_eff = e4m3_decode(s8) * g;
+        const float r = 1.0f / s_eff;
+        const bool zero = bad || s_eff == 0.0f;
+        if (r <= 3.0e38f) {                       // finite r: every y * r is a number
+#pragma unroll
+          for (int k = 0; k < BS / 2; ++k) w[k >> 2] = cvt_pair(w[k >> 2], y[2 * k] * r, y[2 * k + 1] * r, k & 3);
+        } else {                                  // s_eff below 2^-128: 0 * inf is NaN -> code 0
+#pragma unroll
+          for (int k = 0; k < BS; ++k) w[k >> 3] |= e2m1_code_nan0(y[k] * r) << (4 * (k & 7));
+        }
+        if (zero) zero_words(w);
+        reinterpret_cast<uint8_t*>(scales)[row * nblk + blk] = bad ? 0x7fu : static_cast<uint8_t>(s8);
+      } else {  // INT4
+        const float a = __uint_as_float(ab);
+        const _Float16 h = static_cast<_Float16>(a / 7.0f);        // RNE
+        const float s32 = static_cast<float>(h);
+        const float r = 1.0f / s32;
+        const bool zero = bad || s32 == 0.0f;
+        // clamp to [-7, 7], then add 1.5 * 2^23: the fp32 add rounds to the nearest
+        // integer (ties to even) and leaves q in the low mantissa bits (two's complement)
+#pragma unroll
+        for (int k = 0; k < BS; ++k) {
+          const float t = __builtin_amdgcn_fmed3f(y[k] * r, -7.0f, 7.0f) + 12582912.0f;
+          w[k >> 3] |= (__float_as_uint(t) & 15u) << (4 * (k & 7));
+        }
+        if (zero) zero_words(w);
+        uint16_t hb;
+        __builtin_memcpy(&hb, &h, 2);
+        reinterpret_cast<uint16_t*>(scales)[row * nblk + blk] = bad ? static_cast<uint16_t>(0x7e00u) : hb;
+      }
+      store_codes<BS>(codes + row * (d_in / 2) + static_cast<size_t>(blk) * (BS / 2), w);
+    }
+    tok = tok_next;
+    if (tok_base + (it + 1) * kWave >= n) break;  // wave-uniform early exit
+  }
+
+  if constexpr (FMT == kAmax) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) run_max = max(run_max, static_cast<uint32_t>(__shfl_xor(static_cast<int>(run_max), off)));
+    if (lane == 0) atomicMax(amax_out, run_max);
+  }
+}
+
+__global__ void fill_u32(uint32_t* p, uint32_t v) { *p = v; }
+
+using KernelFn = void (*)(const void*, const float*, int, int, float, uint8_t*, void*, uint32_t*);
+
+template <int BS, int FMT>
+KernelFn pick(bool bf16, bool ident) {
+  if (bf16) return ident ? tq_kernel<BS, FMT, true, true> : tq_kernel<BS, FMT, true, false>;
+  return ident ? tq_kernel<BS, FMT, false, true> : tq_kernel<BS, FMT, false, false>;
+}
+
+KernelFn select_kernel(int fmt, int bs, bool bf16, bool ident) {
+  if (bs == 32) {
+    switch (fmt) {
+      case kMX: return pick<32, kMX>(bf16, ident);
+      case kI4: return pick<32, kI4>(bf16, ident);
+      case kAmax: return pick<32, kAmax>(bf16, ident);
+    }
+  } else if (bs == 16) {
+    switch (fmt) {
+      case kNV: return pick<16, kNV>(bf16, ident);
+      case kAmax: return pick<16, kAmax>(bf16, ident);
+    }
+  }
+  return nullptr;
+}
+
+wush_status launch(int fmt, int bs, bool bf16, int n, int d_in, const void* X, const float* T, float g,
+                   uint8_t* codes, void* scales, uint32_t* amax, hipStream_t stream) {
+  if (n == 0) return WUSH_OK;
+  KernelFn k = select_kernel(fmt, bs, bf16, T == nullptr);
+  if (!k) return wush::fail(WUSH_E_UNSUPPORTED, "transform_quant: no kernel for fmt=%d bs=%d", fmt, bs);
+  const int nblk = d_in / bs;
+  dim3 grid((nblk + kWavesPerGroup - 1) / kWavesPerGroup, (n + kWave * kTileIters - 1) / (kWave * kTileIters));
+  if (grid.y > 65535u) return wush::fail(WUSH_E_SHAPE, "transform_quant: n=%d too large", n);
+  hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, T, n, d_in, g, codes, scales, amax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "transform_quant launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+// max|T x| over a tensor, written to a device uint (float bits).
+wush_status tensor_amax(int bs, bool bf16, int n, int d_in, const void* X, const float* T, uint32_t* amax_dev,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(fill_u32, dim3(1), dim3(1), 0, stream, amax_dev, 0u);
+  return launch(kAmax, bs, bf16, n, d_in, X, T, 0.0f, nullptr, nullptr, amax_dev, stream);
+}
+
+wush_status global_scale(int bs, bool bf16, int n, int d_in, const void* X, const float* T, float* g_out,
+                         hipStream_t stream) {
+  uint32_t* dbuf = nullptr;
+  if (hipMalloc(&dbuf, sizeof(uint32_t)) != hipSuccess) return wush::fail(WUSH_E_HIP, "global_scale: hipMalloc failed");
+  wush_status st = tensor_amax(bs, bf16, n, d_in, X, T, dbuf, stream);
+  uint32_t bits = 0;
+  if (st == WUSH_OK) {
+    if (hipMemcpyAsync(&bits, dbuf, sizeof bits, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      st = wush::fail(WUSH_E_HIP, "global_scale: copy back failed");
+  }
+  (void)hipFree(dbuf);
+  if (st != WUSH_OK) return st;
+  float amax;
+  __builtin_memcpy(&amax, &bits, 4);
+  if (!(amax > 0.0f) || bits >= 0x7f800000u)
+    return wush::fail(WUSH_E_NUMERIC, "global_scale: tensor maximum is zero or not finite");
+  *g_out = amax / 2688.0f;   // 6 * 448
+  return WUSH_OK;
+}
+
+wush_status check_common(const char* who, wush_format fmt, int rows, int d_in, const void* X, uint8_t* codes,
+                         void* scales) {
+  const int bs = wush_format_block(fmt);
+  if (bs == 0) return wush::fail(WUSH_E_ARG, "%s: bad format %d", who, static_cast<int>(fmt));
+  if (rows < 0 || d_in < bs || d_in % bs != 0)
+    return wush::fail(WUSH_E_SHAPE, "%s: need rows >= 0 and d_in a positive multiple of %d (rows=%d d_in=%d)", who,
+                      bs, rows, d_in);
+  if (rows > 0 && (!X || !codes || !scales)) return wush::fail(WUSH_E_ARG, "%s: null pointer", who);
+  if (!wush::aligned16(X) || !wush::aligned16(codes))
+    return wush::fail(WUSH_E_ARG, "%s: X and codes must be 16-byte aligned", who);
+  return WUSH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+wush_status wush_transform_quant(wush_format fmt, wush_dtype xdt, int n, int d_in, const void* X, const float* Tx,
+                                 float g, uint8_t* codes, void* scales, void* stream) {
+  wush_status st = check_common("wush_transform_quant", fmt, n, d_in, X, codes, scales);
+  if (st != WUSH_OK) return st;
+  if (xdt != WUSH_F32 && xdt != WUSH_BF16) return wush::fail(WUSH_E_ARG, "wush_transform_quant: bad dtype");
+  if (fmt == WUSH_NVFP4 && !(g > 0.0f && g < 3.0e38f))
+    return wush::fail(WUSH_E_ARG, "wush_transform_quant: NVFP4 needs a positive finite tensor scale g");
+  const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
+  return launch(fk, wush_format_block(fmt), xdt == WUSH_BF16, n, d_in, X, Tx, g, codes, scales, nullptr,
+                static_cast<hipStream_t>(stream));
+}
+
+wush_status wush_nvfp4_global_scale(wush_dtype xdt, int n, int d_in, const void* X, const float* Tx, float* g_out,
+                                    void* stream) {
+  if (!X || !g_out) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale: null pointer");
+  if (xdt != WUSH_F32 && xdt != WUSH_BF16) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale: bad dtype");
+  if (n < 1 || d_in < 16 || d_in % 16 != 0)
+    return wush::fail(WUSH_E_SHAPE, "wush_nvfp4_global_scale: need n >= 1 and d_in %% 16 == 0");
+  if (!wush::aligned16(X)) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale: X must be 16-byte aligned");
+  return global_scale(16, xdt == WUSH_BF16, n, d_in, X, Tx, g_out, static_cast<hipStream_t>(stream));
+}
+
+wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float* W, const float* Tw, uint8_t* codes,
+                              void* scales, float* g_out, void* stream) {
+  wush_status st = check_common("wush_pack_weights", fmt, d_out, d_in, W, codes, scales);
+  if (st != WUSH_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float g = 0.0f;
+  if (fmt == WUSH_NVFP4) {
+    if (!g_out) return wush::fail(WUSH_E_ARG, "wush_pack_weights: NVFP4 needs g_out");
+    if (d_out < 1) return wush::fail(WUSH_E_SHAPE, "wush_pack_weights: NVFP4 needs d_out >= 1");
+    st = global_scale(16, false, d_out, d_in, W, Tw, &g, s);
+    if (st != WUSH_OK) return st;
+    *g_out = g;
+  } else if (g_out) {
+    *g_out = 1.0f;
+  }
+  const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
+  return launch(fk, wush_format_block(fmt), false, d_out, d_in, W, Tw, g, codes, scales, nullptr, s);
+}
+
+}  // extern "C"

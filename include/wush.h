@@ -1,0 +1,216 @@
+/*
+ * wush.h - C ABI of libwush: data-aware block transforms (WUSH) followed by
+ * low-bit block quantization and a W4A4 matmul, native to AMD Instinct MI355X
+ * (gfx950 / CDNA4).
+ *
+ * Sources (web pages, cited by title and section):
+ *  [WUSH-news]  "WUSH" news article (chain.bitekongjian.com): paragraphs on
+ *               the construction, on optimality, on experiments (MXFP4,
+ *               NVFP4, INT4) and on the deployment workflow.
+ *  [WUSH-radio] "WUSH: Near-Optimal Adaptive Transforms for LLM
+ *               Quantization" (AI Radio episode): "Problem Setup and Goal"
+ *               (layer loss), "The gist" (fused GPU implementation).
+ *  [ITQ3_S]     ITQ3_S article (ai.866data.com): "Core technique: FWHT
+ *               pre-rotation" section.
+ *
+ * Conventions shared by every call
+ *  - Layouts are row-major.  Weights use the nn.Linear layout Wt[d_out][d_in]
+ *    (the transpose of the pages' W, which is d_in x d_out); activations are
+ *    token-major Xt[n][d_in] (the transpose of the pages' X).  Block b covers
+ *    input channels [b*bs, (b+1)*bs); transforms and quantization groups both
+ *    run along d_in (the reduction dimension K of the matmul).
+ *  - Packed 4-bit codes: byte j of a row holds element 2j in its low nibble
+ *    and element 2j+1 in its high nibble.
+ *  - The caller owns every buffer.  "Device" pointers are plain HIP device
+ *    allocations (for example torch tensors' data_ptr()); "host" pointers are
+ *    ordinary CPU memory.  Device pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Device calls are asynchronous on that stream unless stated otherwise;
+ *    faults during execution surface at the caller's next synchronisation.
+ *  - Every call validates its arguments before launching anything and returns
+ *    a wush_status; nothing aborts or throws across the ABI.  The thread-local
+ *    string returned by wush_last_error() describes the most recent failure.
+ *  - Calls keep no global mutable state besides that string and are safe to
+ *    call from several threads on different streams.
+ */
+#ifndef WUSH_H
+#define WUSH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WUSH_OK = 0,
+  WUSH_E_ARG = 1,          /* null pointer, bad enum, misaligned pointer   */
+  WUSH_E_SHAPE = 2,        /* sizes that do not divide / exceed limits      */
+  WUSH_E_NUMERIC = 3,      /* Cholesky failed after damping; non-finite g   */
+  WUSH_E_HIP = 4,          /* a HIP runtime call or launch failed           */
+  WUSH_E_UNSUPPORTED = 5   /* valid request this build does not implement   */
+} wush_status;
+
+/* Block formats named for the experiments of [WUSH-news]. */
+typedef enum {
+  WUSH_MXFP4 = 0,  /* 32 E2M1 values + one E8M0 scale byte                    */
+  WUSH_NVFP4 = 1,  /* 16 E2M1 values + one E4M3 scale byte, fp32 tensor scale */
+  WUSH_INT4 = 2    /* 32 symmetric int4 values in [-7,7] + one fp16 scale     */
+} wush_format;
+
+/* Transform families compared in [WUSH-news] (experiments paragraph). */
+typedef enum {
+  WUSH_IDENTITY = 0,
+  WUSH_HADAMARD = 1,  /* orthonormal Sylvester Hadamard H/sqrt(bs)        */
+  WUSH_WUS = 2,       /* S^{1/2} U^T W'^{-1} (no Hadamard factor)          */
+  WUSH_WUSH = 3       /* H/sqrt(bs) S^{1/2} U^T W'^{-1}                    */
+} wush_kind;
+
+typedef enum { WUSH_F32 = 0, WUSH_BF16 = 1 } wush_dtype;
+
+/* Block size of a format: 32 (MXFP4, INT4) or 16 (NVFP4); 0 for a bad value. */
+int wush_format_block(wush_format fmt);
+
+/* ------------------------------------------------------------------------
+ * Offline, host (CPU, fp64 inside, synchronous; no device memory touched).
+ * ---------------------------------------------------------------------- */
+
+/* Activation second moments per block, [WUSH-news] deployment paragraph
+ * (moments come from calibration data):  Sx[b] = X_b X_b^T / n.
+ *   X   host, [n][d_in] fp32 (token-major calibration activations).
+ *   Sx  host out, [d_in/bs][bs][bs] fp32 (accumulated in fp64, rounded once).
+ * Errors: WUSH_E_ARG (null), WUSH_E_SHAPE (n < 1, bs not 16/32, d_in % bs). */
+wush_status wush_block_moments(int bs, int n, int d_in, const float* X, float* Sx);
+
+/* Per-block transform pair, [WUSH-news] construction paragraph (Cholesky
+ * factor of weight statistics, U and S of an SVD, Hadamard) and deployment
+ * paragraph (per block, in parallel).  For every block b:
+ *   A_b = W_b W_b^T (fp64, summed over the d_out rows),  A_b = W' W'^T,
+ *   C_b = W'^T Sx_b W' = U diag(lambda) U^T (lambda descending, each column
+ *   of U signed so its largest-magnitude entry is positive), S = sqrt(lambda),
+ *   T_W = Q S^{1/2} U^T W'^{-1},  T_X = Q S^{-1/2} U^T W'^T = T_W^{-T},
+ *   with Q = H/sqrt(bs) for WUSH and Q = I for WUS.  IDENTITY and HADAMARD
+ *   ignore W and Sx (which may then be NULL).  If A_b is not positive
+ *   definite the Cholesky is retried on A_b + eps*(tr A_b/bs)*I for
+ *   eps = 1e-10, 1e-8, 1e-6, 1e-4, 1e-2; sigma_i is floored at 1e-12*sigma_1.
+ *   W   host, [d_out][d_in] fp32.        Sx  host, [d_in/bs][bs][bs] fp32.
+ *   Tx, Tw  host out, [d_in/bs][bs][bs] fp32 row-major (y = T x per block).
+ * Errors: WUSH_E_ARG, WUSH_E_SHAPE (bs not 16/32, d_in % bs), WUSH_E_NUMERIC
+ * (a block still not positive definite after the damping ladder). */
+wush_status wush_build_transforms(wush_kind kind, int bs, int d_in, int d_out,
+                                  const float* W, const float* Sx, float* Tx, float* Tw);
+
+/* ------------------------------------------------------------------------
+ * Device calls (HIP, gfx950).
+ * ---------------------------------------------------------------------- */
+
+/* Transform then quantize activations: the online step of [WUSH-news]
+ * (deployment paragraph: only activations are transformed at inference),
+ * fused as in [WUSH-radio] "The gist".  Per token and block:
+ *   y_i = fma chain over k ascending from +0 of T[i][k]*x[k] (fp32; T == NULL
+ *   means the identity transform, a bit-exact copy), then the block quantizer:
+ *   MXFP4: a = max|y|, e = clamp(floor(log2 a) - 2, -127, 127) (a == 0 -> -127),
+ *          scale byte e+127, codes E2M1(y * 2^-e);
+ *   NVFP4: s8 = E4M3(min(f32(a / f32(6g)), 448)), s = f32(dec(s8) * g),
+ *          codes E2M1(f32(y * f32(1/s))) (all 0 if s == 0);
+ *   INT4:  s16 = fp16(f32(a/7)), codes clamp(rint(f32(y * f32(1/s16))), -7, 7) & 15
+ *          (all 0 if s16 == 0).
+ *   E2M1 rounds to nearest, ties to the even code, saturates at 6 and copies the
+ *   sign bit.  A block with a NaN/Inf value gets the format's NaN scale (0xFF,
+ *   0x7F, 0x7E00) and all-zero codes.
+ *   X       device, [n][d_in] fp32 or bf16 (xdt).
+ *   Tx      device, [d_in/bs][bs][bs] fp32, or NULL for identity.
+ *   g       NVFP4 per-tensor fp32 scale (> 0, finite); ignored otherwise.
+ *   codes   device out, [n][d_in/2] bytes.
+ *   scales  device out, [n][d_in/bs]: uint8 (MXFP4, NVFP4) or uint16 fp16 bits (INT4).
+ * Errors: WUSH_E_ARG, WUSH_E_SHAPE (n < 0, d_in % bs), WUSH_E_HIP. */
+wush_status wush_transform_quant(wush_format fmt, wush_dtype xdt, int n, int d_in,
+                                 const void* X, const float* Tx, float g,
+                                 uint8_t* codes, void* scales, void* stream);
+
+/* NVFP4 per-tensor scale of transformed data: g = f32(max|T x| / 2688)
+ * (2688 = 6 * 448, the largest E2M1 value times the largest E4M3 value).
+ * Used on calibration activations; the weight path computes it itself.
+ * Synchronises `stream`; *g_out is a host pointer.  bs is 16.
+ * Errors: WUSH_E_ARG, WUSH_E_SHAPE, WUSH_E_HIP, WUSH_E_NUMERIC (non-finite
+ * or zero maximum). */
+wush_status wush_nvfp4_global_scale(wush_dtype xdt, int n, int d_in, const void* X,
+                                    const float* Tx, float* g_out, void* stream);
+
+/* Transform and quantize weights offline ([WUSH-news] deployment paragraph:
+ * weights are transformed once, after training): the same arithmetic as
+ * wush_transform_quant with T_W applied to every weight row.  For NVFP4 the
+ * per-tensor scale is computed first (wush_nvfp4_global_scale on the rows)
+ * and written to *g_out (host pointer; the call then synchronises `stream`);
+ * g_out may be NULL for the other formats.
+ *   W       device, [d_out][d_in] fp32.     Tw  device, [d_in/bs][bs][bs] fp32 or NULL.
+ *   codes   device out, [d_out][d_in/2].    scales  device out, [d_out][d_in/bs]. */
+wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float* W,
+                              const float* Tw, uint8_t* codes, void* scales,
+                              float* g_out, void* stream);
+
+/* W4A4 matmul, the "FP4 MatMul" of [WUSH-radio]:
+ *   Y[m][j] = sum_k dec(A)[m][k] * dec(B)[j][k],  fp32 output, fp32 accumulation.
+ * dec() multiplies each code by its block scale (and by a_g / b_g for NVFP4).
+ *   A: a_codes [M][K/2], a_scales [M][K/bs]  (activations, from wush_transform_quant)
+ *   B: b_codes [N][K/2], b_scales [N][K/bs]  (weights, from wush_pack_weights)
+ *   Y: device out, [M][N] fp32.
+ * MXFP4 runs on the gfx950 block-scaled FP4 matrix cores; NVFP4 and INT4 use
+ * exact dequantization to bf16 / int8 matrix cores with per-block scaling.
+ * Errors: WUSH_E_ARG, WUSH_E_SHAPE (M, N < 1; K < 1 or K % 128), WUSH_E_HIP. */
+wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K,
+                           const uint8_t* a_codes, const void* a_scales, float a_g,
+                           const uint8_t* b_codes, const void* b_scales, float b_g,
+                           float* Y, void* stream);
+
+/* Layer loss of [WUSH-radio] "Problem Setup and Goal":
+ *   *loss = sum over M x N of (Yhat - Yref)^2 / (M * N), accumulated in fp64
+ *   with a fixed two-stage reduction order (deterministic).
+ *   Yhat, Yref device, [M][N] fp32; loss device out (one double);
+ *   ws device workspace of wush_loss_ws_bytes(M, N) bytes. */
+wush_status wush_layer_loss(int M, int N, const float* Yhat, const float* Yref,
+                            double* loss, void* ws, void* stream);
+size_t wush_loss_ws_bytes(int M, int N);
+
+/* ------------------------------------------------------------------------
+ * Hadamard-256 3-bit weight-only path ([ITQ3_S], core-technique section:
+ * 256-point Walsh-Hadamard pre-rotation before a uniform 3-bit quantizer,
+ * inverse rotation when weights are loaded for the matmul).
+ * ---------------------------------------------------------------------- */
+
+/* Per 256-vector of every weight row: fp32 FWHT with butterfly stages
+ * h = 1, 2, ..., 128, then * 1/16; a = max|v|; s16 = fp16(f32(a/3));
+ * q = clamp(rint(f32(v * f32(1/s16))), -3, 3) (all 0 if s16 == 0).
+ *   W       device, [d_out][d_in] fp32, d_in % 256 == 0.
+ *   planes  device out, [d_out][d_in/256][96]: bytes 0-63 hold bits 0-1 of
+ *           code k (= q & 7) at byte k/4, bit 2*(k%4); bytes 64-95 hold bit 2
+ *           of code k at byte 64 + k/8, bit k%8.
+ *   scales  device out, [d_out][d_in/256] fp16 bits. */
+wush_status wush_had256_pack_weights(int d_out, int d_in, const float* W,
+                                     uint8_t* planes, uint16_t* scales, void* stream);
+
+/* y[b][j] = sum_k x[b][k] * w_hat[j][k] with w_hat = s16 * (H_256 q) / 16 per
+ * 256-vector (the inverse rotation of the dequantized codes).
+ *   x       device, [batch][d_in] bf16 bits.   y  device out, [batch][d_out] fp32.
+ * Errors: WUSH_E_SHAPE (batch not in 1..16, d_in % 256), WUSH_E_ARG, WUSH_E_HIP. */
+wush_status wush_had256_gemv(int batch, int d_out, int d_in, const uint16_t* x,
+                             const uint8_t* planes, const uint16_t* scales,
+                             float* y, void* stream);
+
+/* Unquantized rotation v = H_256 w / 16 per 256-vector, in place allowed
+ * (in == out).  H/16 is orthogonal and its own inverse, so two calls return
+ * the input exactly on integer data with |w| <= 2^15 ([ITQ3_S] round trip).
+ *   in, out  device, [rows][d_in] fp32, d_in % 256 == 0. */
+wush_status wush_had256_rotate(int rows, int d_in, const float* in, float* out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+const char* wush_status_string(wush_status s);
+const char* wush_last_error(void);
+/* Library version string, e.g. "wush 0.1 gfx950". */
+const char* wush_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WUSH_H */

@@ -76,7 +76,9 @@ def e2m1_code(v):
     magnitude 0.  NaN encodes as 0.
     """
     v = np.asarray(v, dtype=np.float64)
-    mag = np.abs(v)
+    # every magnitude at or above 6 saturates to 6; clamping to 8 first keeps the
+    # distances to the grid resolvable in fp64 for huge values and infinities
+    mag = np.minimum(np.abs(v), 8.0)
     d = np.abs(mag[..., None] - E2M1_MAG)           # distance to every level
     dmin = d.min(axis=-1, keepdims=True)
     cand = d == dmin                                  # one or two nearest levels

@@ -1,0 +1,151 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+rejects bad arguments before touching the GPU, and its host-side builder and
+moment accumulation agree with the oracle."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wush.h")
+
+W = pytest.importorskip("aware_block_transforms_amd._lib")
+from oracle import transforms as tr  # noqa: E402
+from synth.gen import random_case, CONFIGS, make_weights, make_activations  # noqa: E402
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wush_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(W.lib, name), name
+    # and the binding wraps each of them
+    assert set(names) <= set(W.EXPORTED), set(names) - set(W.EXPORTED)
+
+
+def test_status_strings_and_version():
+    assert W.lib.wush_status_string(0) == b"ok"
+    assert W.lib.wush_status_string(3) == b"numerical failure"
+    assert W.wush_version().startswith("wush")
+    assert W.lib.wush_format_block(0) == 32 and W.lib.wush_format_block(1) == 16
+    assert W.lib.wush_format_block(2) == 32 and W.lib.wush_format_block(7) == 0
+
+
+def test_device_calls_reject_bad_arguments_before_launch():
+    L = W.lib
+    # null pointers / bad shapes / bad enums: validated on the host, no HIP call made
+    assert L.wush_transform_quant(0, 0, 4, 64, None, None, 0.0, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_transform_quant(0, 0, 4, 63, None, None, 0.0, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_transform_quant(9, 0, 4, 64, None, None, 0.0, None, None, None) == W.WUSH_E_ARG
+    assert b"format" in L.wush_last_error()
+    assert L.wush_w4a4_gemm(0, 4, 4, 100, None, None, 1.0, None, None, 1.0, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_w4a4_gemm(0, 4, 4, 128, None, None, 1.0, None, None, 1.0, None, None) == W.WUSH_E_ARG
+    assert L.wush_w4a4_gemm(0, 0, 4, 128, None, None, 1.0, None, None, 1.0, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_layer_loss(0, 4, None, None, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_had256_gemv(17, 4, 256, None, None, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_had256_pack_weights(4, 100, None, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_had256_rotate(4, 256, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_loss_ws_bytes(10, 10) >= 8
+    # misaligned pointer
+    buf = np.zeros(64, np.uint8)
+    assert L.wush_transform_quant(0, 0, 1, 32, buf.ctypes.data + 1, None, 0.0, buf.ctypes.data, buf.ctypes.data,
+                                  None) == W.WUSH_E_ARG
+    # NVFP4 needs a positive finite tensor scale
+    assert L.wush_transform_quant(1, 0, 1, 32, buf.ctypes.data, None, 0.0, buf.ctypes.data, buf.ctypes.data,
+                                  None) == W.WUSH_E_ARG
+
+
+def test_builder_rejects_bad_input():
+    T = np.zeros((2, 32, 32), np.float32)
+    with pytest.raises(W.WushError) as e:
+        W.wush_build_transforms("wush", 32, None, None, T, T.copy())
+    assert e.value.status == W.WUSH_E_ARG
+    Wt = np.zeros((4, 64), np.float32)
+    with pytest.raises(W.WushError) as e:
+        W.wush_build_transforms("wush", 24, Wt, np.zeros((2, 32, 32), np.float32), T, T.copy())
+    assert e.value.status == W.WUSH_E_SHAPE
+
+
+def test_builder_damps_rank_deficient_blocks_like_the_oracle():
+    rng = np.random.default_rng(3)
+    Wt = rng.standard_normal((8, 64)).astype(np.float32)       # 8 rows: rank-deficient 32x32 moments
+    X = rng.standard_normal((100, 64)).astype(np.float32)
+    Sx = tr.activation_moments(X, 32).astype(np.float32)
+    Tx = np.empty((2, 32, 32), np.float32)
+    Tw = np.empty_like(Tx)
+    W.wush_build_transforms("wush", 32, Wt, Sx, Tx, Tw)
+    _, _, tx64, tw64 = tr.build_transforms("wush", Wt, Sx, 32)
+    for b in range(2):
+        assert np.allclose(Tw[b].astype(np.float64).T @ Tx[b].astype(np.float64), np.eye(32), atol=1e-3)
+    assert np.allclose(Tx, tx64, rtol=1e-3, atol=1e-3 * np.abs(tx64).max())
+
+
+def test_builder_zero_weights_is_numeric_error():
+    Wt = np.zeros((16, 32), np.float32)
+    Sx = np.eye(32, dtype=np.float32)[None]
+    T = np.empty((1, 32, 32), np.float32)
+    with pytest.raises(W.WushError) as e:
+        W.wush_build_transforms("wush", 32, Wt, Sx, T, T.copy())
+    assert e.value.status == W.WUSH_E_NUMERIC
+
+
+def test_moments_match_oracle():
+    _, X = random_case(21, 300, 128, 8)
+    for bs in (16, 32):
+        Sx = np.empty((128 // bs, bs, bs), np.float32)
+        W.wush_block_moments(bs, X, Sx)
+        ref = tr.activation_moments(X, bs)
+        assert np.allclose(Sx, ref, rtol=2e-7, atol=1e-7 * np.abs(ref).max())
+        assert np.array_equal(Sx, Sx.transpose(0, 2, 1))
+
+
+def _t_tolerance(T, ref):
+    # the two builders round the same fp64 matrix to fp32 from slightly different
+    # fp64 values (Jacobi vs LAPACK eigh, different summation orders); allow a
+    # few fp32 ulps of the block's largest entry
+    return 8 * 2.0 ** -24 * np.abs(ref).max(axis=(1, 2), keepdims=True)
+
+
+@pytest.mark.parametrize("kind", ["identity", "hadamard", "wus", "wush"])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_builder_matches_oracle(kind, bs):
+    Wt, X = random_case(22 + bs, 400, 256, 96)
+    Sx = tr.activation_moments(X, bs).astype(np.float32)
+    nblk = 256 // bs
+    Tx = np.empty((nblk, bs, bs), np.float32)
+    Tw = np.empty_like(Tx)
+    W.wush_build_transforms(kind, bs, Wt, Sx, Tx, Tw)
+    rx, rw, _, _ = tr.build_transforms(kind, Wt, Sx, bs)
+    if kind in ("identity", "hadamard"):
+        assert np.array_equal(Tx, rx) and np.array_equal(Tw, rw)
+        return
+    assert np.all(np.abs(Tx - rx) <= _t_tolerance(Tx, rx)), np.abs(Tx - rx).max()
+    assert np.all(np.abs(Tw - rw) <= _t_tolerance(Tw, rw)), np.abs(Tw - rw).max()
+    # proxy loss equal to the closed form to high accuracy
+    A = tr.weight_moments(Wt, bs)
+    for b in range(nblk):
+        j_c = tr.proxy_loss(Tw[b].astype(np.float64), A[b], Sx[b].astype(np.float64))
+        j_o = tr.proxy_loss(rw[b].astype(np.float64), A[b], Sx[b].astype(np.float64))
+        assert np.isclose(j_c, j_o, rtol=1e-5)
+
+
+def test_builder_on_tiny_workload():
+    w = CONFIGS["tiny"]
+    Wt = make_weights(w)
+    X = make_activations(w)
+    Sx = np.empty((8, 32, 32), np.float32)
+    W.wush_block_moments(32, X, Sx)
+    Tx = np.empty((8, 32, 32), np.float32)
+    Tw = np.empty_like(Tx)
+    W.wush_build_transforms("wush", 32, Wt, Sx, Tx, Tw)
+    rx, rw, _, _ = tr.build_transforms("wush", Wt, tr.activation_moments(X, 32).astype(np.float32), 32)
+    assert np.all(np.abs(Tx - rx) <= _t_tolerance(Tx, rx) + 4 * 2.0 ** -24 * np.abs(rx).max())

@@ -1,0 +1,216 @@
+"""GPU parity of every libwush device call against the oracle (small and ragged sizes).
+
+Codes and scales must match bit-exactly; matmul outputs and the loss within
+the relative tolerance 1e-3 (per element, against max(|ref|, rms(ref))).
+The oracle builds its own transforms, codes and outputs from the seeded
+inputs; nothing it consumes comes from the GPU.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import aware_block_transforms_amd as W
+from oracle import quant, transforms as tr, gemm as og, had256 as oh
+from synth.gen import random_case
+from gpu_util import DEV, to_dev, x_dev, host, scales_np, gemm_close
+
+pytestmark = pytest.mark.gpu
+
+SHAPES32 = [(1, 32), (200, 160), (130, 544), (64, 256)]
+SHAPES16 = [(1, 16), (200, 208), (70, 48)]
+
+
+def _oracle_tq(fmt, kind, X, Wt):
+    bs = W.BLOCK[fmt]
+    Sx = tr.activation_moments(X, bs).astype(np.float32)
+    Tx, Tw, _, _ = tr.build_transforms(kind, Wt, Sx, bs)
+    ident = kind == "identity"
+    g = None
+    if fmt == "nvfp4":
+        g = quant.nvfp4_tensor_scale(quant.apply_transform(Tx, X, identity=ident))
+    c, s = quant.transform_quant(fmt, Tx, X, g=g, identity=ident)
+    return Tx, Tw, g, c, s
+
+
+def _gpu_tq(fmt, X, Tx, dtype, g, ident):
+    n, d_in = X.shape
+    bs = W.BLOCK[fmt]
+    codes = torch.empty((n, d_in // 2), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((n, d_in // bs), dtype=torch.int16 if fmt == "int4" else torch.uint8, device=DEV)
+    W.wush_transform_quant(fmt, x_dev(X, dtype), None if ident else to_dev(Tx), codes, sc, g=g or 0.0)
+    torch.cuda.synchronize()
+    return host(codes), scales_np(sc, fmt)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["identity", "hadamard", "wus", "wush"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_transform_quant_bit_exact(fmt, kind, dtype):
+    shapes = SHAPES16 if fmt == "nvfp4" else SHAPES32
+    for si, (n, d_in) in enumerate(shapes):
+        Wt, X = random_case(100 + si, n, d_in, 48, dtype=dtype)
+        Tx, _, g, rc, rs = _oracle_tq(fmt, kind, X, Wt)
+        gc, gs = _gpu_tq(fmt, X, Tx, dtype, g, kind == "identity")
+        assert np.array_equal(gs, rs), (fmt, kind, dtype, n, d_in, np.argwhere(gs != rs)[:5])
+        assert np.array_equal(gc, rc), (fmt, kind, dtype, n, d_in, np.argwhere(gc != rc)[:5])
+
+
+def _edge_inputs(d_in):
+    rng = np.random.default_rng(77)
+    X = rng.standard_normal((9, d_in)).astype(np.float32)
+    X[0] = 0.0                                        # all-zero rows
+    X[1] = -0.0
+    X[2, :16] = np.float32(1e-40)                     # subnormal block
+    X[3, 5] = np.float32(3e37)                        # huge value
+    X[4] *= np.float32(2.0 ** -120)                   # tiny but normal
+    X[5, ::2] = np.float32(6.0 * 2 ** -3)             # exact E2M1 grid points / ties
+    X[5, 1::2] = np.float32(0.25 * 2 ** -3)
+    X[6, 7] = np.nan                                  # NaN block
+    X[7, 17] = np.inf                                 # Inf block
+    X[8, :] = np.float32(1.0)
+    return X
+
+
+@pytest.mark.parametrize("kind", ["identity", "wush"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_transform_quant_edge_cases(fmt, kind):
+    d_in = 64
+    X = _edge_inputs(d_in)
+    Wt, Xcal = random_case(5, 50, d_in, 40)
+    bs = W.BLOCK[fmt]
+    Sx = tr.activation_moments(Xcal, bs).astype(np.float32)
+    Tx, _, _, _ = tr.build_transforms(kind, Wt, Sx, bs)
+    ident = kind == "identity"
+    g = np.float32(0.01) if fmt == "nvfp4" else None
+    with np.errstate(all="ignore"):
+        rc, rs = quant.transform_quant(fmt, Tx, X, g=g, identity=ident)
+    gc, gs = _gpu_tq(fmt, X, Tx, "f32", g, ident)
+    assert np.array_equal(gs, rs), np.argwhere(gs != rs)[:8]
+    assert np.array_equal(gc, rc), np.argwhere(gc != rc)[:8]
+
+
+def test_transform_quant_empty_batch():
+    codes = torch.empty((0, 16), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((0, 1), dtype=torch.uint8, device=DEV)
+    X = torch.empty((0, 32), dtype=torch.float32, device=DEV)
+    W.wush_transform_quant("mxfp4", X, None, codes, sc)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nvfp4_global_scale(dtype):
+    Wt, X = random_case(7, 150, 96, 32, dtype=dtype)
+    Sx = tr.activation_moments(X, 16).astype(np.float32)
+    Tx, _, _, _ = tr.build_transforms("wush", Wt, Sx, 16)
+    ref = quant.nvfp4_tensor_scale(quant.apply_transform(Tx, X))
+    g = W.wush_nvfp4_global_scale(x_dev(X, dtype), to_dev(Tx))
+    assert np.float32(g).view(np.uint32) == np.float32(ref).view(np.uint32)
+
+
+@pytest.mark.parametrize("kind", ["identity", "wush"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_pack_weights_bit_exact(fmt, kind):
+    Wt, X = random_case(8, 300, 160 if fmt != "nvfp4" else 176, 77)
+    bs = W.BLOCK[fmt]
+    Sx = tr.activation_moments(X, bs).astype(np.float32)
+    _, Tw, _, _ = tr.build_transforms(kind, Wt, Sx, bs)
+    ident = kind == "identity"
+    g = None
+    if fmt == "nvfp4":
+        g = quant.nvfp4_tensor_scale(quant.apply_transform(Tw, Wt, identity=ident))
+    rc, rs = quant.transform_quant(fmt, Tw, Wt, g=g, identity=ident)
+    d_out, d_in = Wt.shape
+    codes = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((d_out, d_in // bs), dtype=torch.int16 if fmt == "int4" else torch.uint8, device=DEV)
+    gg = W.wush_pack_weights(fmt, to_dev(Wt), None if ident else to_dev(Tw), codes, sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(scales_np(sc, fmt), rs)
+    assert np.array_equal(host(codes), rc)
+    if fmt == "nvfp4":
+        assert np.float32(gg) == g
+
+
+GEMM_SHAPES = [(16, 16, 128), (128, 256, 256), (100, 70, 384), (257, 129, 640), (64, 512, 1024)]
+
+
+def _rand_operands(fmt, M, N, K, seed):
+    rng = np.random.default_rng([seed, M, N, K])
+    A = (rng.standard_normal((M, K)) * np.exp(rng.uniform(-2, 2, (M, 1)))).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    A[:, rng.choice(K, 3, replace=False)] *= 30
+    ga = gb = None
+    if fmt == "nvfp4":
+        ga, gb = quant.nvfp4_tensor_scale(A), quant.nvfp4_tensor_scale(B)
+    ca, sa = quant.transform_quant(fmt, None, A, g=ga, identity=True)
+    cb, sb = quant.transform_quant(fmt, None, B, g=gb, identity=True)
+    return ca, sa, cb, sb, ga, gb
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_w4a4_gemm(fmt, shape):
+    M, N, K = shape
+    ca, sa, cb, sb, ga, gb = _rand_operands(fmt, M, N, K, 1)
+    ref = og.w4a4_gemm(fmt, ca, sa, cb, sb, ga, gb)
+    Y = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+    W.wush_w4a4_gemm(fmt, to_dev(ca), to_dev(sa), to_dev(cb), to_dev(sb), Y,
+                     a_g=ga or 1.0, b_g=gb or 1.0)
+    torch.cuda.synchronize()
+    ok, worst = gemm_close(host(Y), ref)
+    assert ok, (fmt, shape, worst)
+
+
+def test_layer_loss():
+    rng = np.random.default_rng(3)
+    for M, N in [(1, 1), (3, 5), (128, 256), (333, 77)]:
+        Yh = rng.standard_normal((M, N)).astype(np.float32)
+        Yr = (Yh + rng.standard_normal((M, N)) * 0.1).astype(np.float32)
+        ref = og.layer_loss(Yh, Yr)
+        ws = torch.empty(W.wush_loss_ws_bytes(M, N) // 8, dtype=torch.float64, device=DEV)
+        out = torch.empty(1, dtype=torch.float64, device=DEV)
+        W.wush_layer_loss(to_dev(Yh), to_dev(Yr), out, ws)
+        torch.cuda.synchronize()
+        assert abs(out.item() - ref) <= 1e-3 * ref, (M, N, out.item(), ref)
+        # deterministic: same bits on a second call
+        out2 = torch.empty(1, dtype=torch.float64, device=DEV)
+        W.wush_layer_loss(to_dev(Yh), to_dev(Yr), out2, ws)
+        torch.cuda.synchronize()
+        assert out.item() == out2.item()
+
+
+def test_had256_pack_bit_exact_and_rotate():
+    Wt, _ = random_case(30, 1, 768, 37)
+    planes = torch.empty((37, 3, 96), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((37, 3), dtype=torch.int16, device=DEV)
+    W.wush_had256_pack_weights(to_dev(Wt), planes, sc)
+    rp, rs = oh.pack_weights(Wt)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sc).view(np.uint16), rs)
+    assert np.array_equal(host(planes), rp)
+    # rotation equals the oracle's butterflies bit for bit; two rotations are exact on integers
+    out = torch.empty((37, 768), dtype=torch.float32, device=DEV)
+    W.wush_had256_rotate(to_dev(Wt), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint32), oh.fwht256(Wt.reshape(37, 3, 256)).reshape(37, 768).view(np.uint32))
+    ints = np.random.default_rng(4).integers(-2 ** 15, 2 ** 15 + 1, (5, 512)).astype(np.float32)
+    a = to_dev(ints)
+    W.wush_had256_rotate(a, a)
+    W.wush_had256_rotate(a, a)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a), ints)
+
+
+@pytest.mark.parametrize("batch", [1, 3, 4, 5, 16])
+def test_had256_gemv(batch):
+    Wt, _ = random_case(31, 1, 1280, 200)
+    rp, rs = oh.pack_weights(Wt)
+    x = np.random.default_rng(batch).standard_normal((batch, 1280)).astype(np.float32)
+    from synth.gen import bf16_round, bf16_bits
+    xb = bf16_round(x)
+    ref = oh.gemv(xb, rp, rs)
+    y = torch.full((batch, 200), np.nan, dtype=torch.float32, device=DEV)
+    W.wush_had256_gemv(to_dev(bf16_bits(xb).view(np.int16)), to_dev(rp), to_dev(rs.view(np.int16)), y)
+    torch.cuda.synchronize()
+    ok, worst = gemm_close(host(y), ref)
+    assert ok, worst

@@ -118,12 +118,13 @@ def test_e2m1_golden_ties():
     with open(os.path.join(GOLDEN, "e2m1_ties.json")) as f:
         g = json.load(f)
     for v, code in g["cases"]:
-        assert int(fp.e2m1_code(np.float64(v))) == code, v
+        assert int(fp.e2m1_code(np.float64(float(v)))) == code, v
 
 
 def test_e2m1_against_thresholds_and_brute_force():
     rng = np.random.default_rng(3)
-    grid = np.concatenate([np.arange(-8, 8.0001, 0.125), [-0.0, 0.0, np.nan, 1e9, -1e9, 1e-30, -1e-30]])
+    grid = np.concatenate([np.arange(-8, 8.0001, 0.125), [-0.0, 0.0, np.nan, 1e9, -1e9, 1e-30, -1e-30],
+                           [1e20, -1e20, 3.4e38, np.inf, -np.inf]])
     vals = np.concatenate([grid, rng.uniform(-9, 9, 5000)])
     codes = fp.e2m1_code(vals)
     dec = fp.e2m1_value(np.arange(16))
@@ -132,7 +133,7 @@ def test_e2m1_against_thresholds_and_brute_force():
         if np.isnan(v):
             continue
         # brute force over all 16 codes: nearest value with the sign of v
-        d = np.abs(v - dec)
+        d = np.abs(min(abs(v), 8.0) * np.sign(v) - dec) if np.isfinite(v) or np.isinf(v) else np.abs(v - dec)
         same_sign = np.array([np.signbit(v) == bool(k & 8) for k in range(16)])
         d = np.where(same_sign, d, np.inf)
         assert d[c] == d.min()
