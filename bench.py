@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Throughput of the WUSH W4A4 layer path on one MI355X.
+
+One step = the online hot path over one batch: transform + quantize the
+activations (wush_transform_quant), then the W4A4 matmul against the
+offline-packed weights (wush_w4a4_gemm).  Inputs are seeded synthetic tensors
+already resident in HBM; to keep the 256 MB Infinity Cache from serving them,
+each step uses the next of `--rotate` copies of the activations and of the
+packed weights.
+
+Prints one JSON line (rank 0, one GPU):
+  value        whole-step layer throughput, 2*M*N*K / step time, in TFLOP/s
+  quant_GBps   algorithmic bytes of transform+quantize / its time
+  roofline     the dominant kernel (the matmul) against the dense MXFP4 peak
+  tq_roofline  transform+quantize against its own bound
+  cpu_baseline the oracle timed on a bounded sample on this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+HBM_GBPS = 8000.0
+MXFP4_TFLOPS = 10100.0      # dense FP4 matrix
+BF16_TFLOPS = 2500.0        # dense bf16 matrix (NVFP4 path)
+INT8_TOPS = 5000.0          # dense int8 matrix (INT4 path)
+# fp32 FMA on the vector ALU without packed math: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+VALU_FP32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+METRIC = "W4A4 layer TFLOPS (transform+quant+GEMM) & quant GB/s, % roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_8b_up",
+                    choices=["qwen3_8b_up", "tiny", "square_sweep", "qwen3_14b", "had256"])
+    ap.add_argument("--fmt", default=None, help="square_sweep: mxfp4 | nvfp4 | int4")
+    ap.add_argument("--kind", default=None, help="square_sweep: identity | hadamard | wus | wush")
+    ap.add_argument("--batch", type=int, default=1, help="had256: batch 1..16")
+    ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- setup
+
+
+class Layer:
+    """One quantized linear layer, device resident, with `rotate` copies of its inputs."""
+
+    def __init__(self, wl, fmt, kind, rotate, W, torch):
+        from synth.gen import make_weights, make_activations, bf16_bits
+        self.wl, self.fmt, self.kind = wl, fmt, kind
+        self.bs = W.BLOCK[fmt]
+        self.M, self.K, self.N = wl.n, wl.d_in, wl.d_out
+        t0 = time.time()
+        Wt = make_weights(wl)
+        X = make_activations(wl)
+        nblk = self.K // self.bs
+        # offline: moments and transforms on the host (library C++ builder)
+        Sx = np.empty((nblk, self.bs, self.bs), np.float32)
+        W.wush_block_moments(self.bs, X, Sx)
+        Tx = np.empty_like(Sx)
+        Tw = np.empty_like(Sx)
+        W.wush_build_transforms(kind, self.bs, Wt if kind in ("wus", "wush") else None,
+                                Sx if kind in ("wus", "wush") else None, Tx, Tw)
+        ident = kind == "identity"
+        dev = "cuda"
+        self.Tx = None if ident else torch.from_numpy(Tx).to(dev)
+        Twd = None if ident else torch.from_numpy(Tw).to(dev)
+        sdt = torch.int16 if fmt == "int4" else torch.uint8
+        Wd = torch.from_numpy(Wt).to(dev)
+        wc = torch.empty((self.N, self.K // 2), dtype=torch.uint8, device=dev)
+        wsc = torch.empty((self.N, nblk), dtype=sdt, device=dev)
+        self.w_g = W.wush_pack_weights(fmt, Wd, Twd, wc, wsc)
+        del Wd
+        if wl.dtype == "bf16":
+            xd = torch.from_numpy(bf16_bits(X).view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            xd = torch.from_numpy(X).to(dev)
+        self.x_g = W.wush_nvfp4_global_scale(xd, self.Tx) if fmt == "nvfp4" else 1.0
+        self.X = [xd] + [xd.clone() for _ in range(rotate - 1)]
+        self.wc = [wc] + [wc.clone() for _ in range(rotate - 1)]
+        self.wsc = [wsc] + [wsc.clone() for _ in range(rotate - 1)]
+        self.xc = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device=dev)
+        self.xsc = torch.empty((self.M, nblk), dtype=sdt, device=dev)
+        self.Y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
+        self.x_elem_bytes = 2 if wl.dtype == "bf16" else 4
+        self.host = (Wt, X, Tx, Tw)
+        self.setup_s = time.time() - t0
+
+    # algorithmic work
+    def tq_bytes(self):
+        el = self.M * self.K
+        sbytes = {"mxfp4": 1.0 / 32, "nvfp4": 1.0 / 16, "int4": 2.0 / 32}[self.fmt]
+        tbytes = 0 if self.kind == "identity" else (self.K // self.bs) * self.bs * self.bs * 4
+        return el * (self.x_elem_bytes + 0.5 + sbytes) + tbytes
+
+    def tq_flops(self):
+        return 0.0 if self.kind == "identity" else 2.0 * self.bs * self.M * self.K
+
+    def gemm_flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def gemm_bytes(self):
+        sb = {"mxfp4": 1.0 / 32, "nvfp4": 1.0 / 16, "int4": 2.0 / 32}[self.fmt]
+        return (self.M + self.N) * self.K * (0.5 + sb) + self.M * self.N * 4
+
+
+def run_layer_steps(layers, W, torch, steps, warmup, rotate):
+    """Warm up, then time `steps` steps; per-kernel HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        r = i % rotate
+        for li, L in enumerate(layers):
+            if ev is not None:
+                ev[li][0].record(stream)
+            W.wush_transform_quant(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
+            if ev is not None:
+                ev[li][1].record(stream)
+            W.wush_w4a4_gemm(L.fmt, L.xc, L.xsc, L.wc[r], L.wsc[r], L.Y, a_g=L.x_g, b_g=L.w_g)
+            if ev is not None:
+                ev[li][2].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # whole-step timing: no per-kernel events inside
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / steps
+    # per-kernel durations: events between launches on the same stream
+    n_ev = min(steps, 50)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(n_ev)]
+    for i in range(n_ev):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    tq_ms = [float(np.mean([evs[i][li][0].elapsed_time(evs[i][li][1]) for i in range(n_ev)])) for li in range(len(layers))]
+    gm_ms = [float(np.mean([evs[i][li][1].elapsed_time(evs[i][li][2]) for i in range(n_ev)])) for li in range(len(layers))]
+    return ms_step, tq_ms, gm_ms
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        n = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+        return int(n)
+    except Exception:
+        return 1
+
+
+def cpu_baseline(L, target_s):
+    """Oracle time for the same step, measured on a bounded sample and scaled to TFLOP/s.
+
+    transform+quantize: `mt` tokens of the real activations with the real transforms;
+    matmul: the oracle's decode + fp64 product of `ms` token rows against `ns` weight
+    rows (those weight codes are prepared by the oracle outside the timed region).
+    Step time = per-token tq time * M + per-flop GEMM time * 2MNK.
+    """
+    from oracle import quant, gemm, transforms
+    Wt, X, _, _ = L.host
+    ident = L.kind == "identity"
+    # the oracle builds its own transforms (untimed)
+    Sx = transforms.activation_moments(X, L.bs).astype(np.float32)
+    Tx, Tw, _, _ = transforms.build_transforms(L.kind, Wt, Sx, L.bs)
+    g = None
+    if L.fmt == "nvfp4":
+        g = L.x_g
+    # size the sample to roughly target_s seconds of work (calibrate on a small run)
+    mt = 8
+    t0 = time.perf_counter()
+    quant.transform_quant(L.fmt, Tx, X[:mt], g=g, identity=ident)
+    per_tok = (time.perf_counter() - t0) / mt
+    mt = int(max(8, min(L.M, 0.5 * target_s / max(per_tok, 1e-9))))
+    t0 = time.perf_counter()
+    ca, sa = quant.transform_quant(L.fmt, Tx, X[:mt], g=g, identity=ident)
+    t_tq = time.perf_counter() - t0
+    ns = min(L.N, 1024)
+    wg = None
+    if L.fmt == "nvfp4":
+        wg = L.w_g
+    cw, sw = quant.transform_quant(L.fmt, Tw, Wt[:ns], g=wg, identity=ident)   # untimed prep
+    ms = min(mt, 256)
+    t0 = time.perf_counter()
+    gemm.w4a4_gemm(L.fmt, ca[:ms], sa[:ms], cw, sw, g, wg)
+    t_g0 = time.perf_counter() - t0
+    reps = int(max(1, min(50, 0.5 * target_s / max(t_g0, 1e-9))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gemm.w4a4_gemm(L.fmt, ca[:ms], sa[:ms], cw, sw, g, wg)
+    t_g = (time.perf_counter() - t0) / reps
+    per_flop = t_g / (2.0 * ms * ns * L.K)
+    step_s = (t_tq / mt) * L.M + per_flop * L.gemm_flops()
+    return {
+        "value": L.gemm_flops() / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cpu_threads(),
+        "kind": "oracle",
+        "sample": (f"transform+quantize of {mt} of {L.M} tokens ({t_tq:.1f} s); decode+fp64 matmul of "
+                   f"{ms} tokens x {ns} weight rows x K={L.K} ({reps} reps, {t_g:.2f} s each); "
+                   f"scaled to the full {L.M}x{L.N}x{L.K} step ({step_s:.0f} s)"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+# ----------------------------------------------------------------------------- main
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import aware_block_transforms_amd as W
+    from synth.gen import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.workload == "had256":
+        return bench_had256(args, W, torch)
+
+    if args.workload == "qwen3_14b":
+        wls = [CONFIGS["qwen3_14b_up"], CONFIGS["qwen3_14b_down"]]
+    else:
+        wls = [CONFIGS[args.workload]]
+    fmt = args.fmt or wls[0].formats[0]
+    kind = args.kind or ("wush" if "wush" in wls[0].kinds else wls[0].kinds[-1])
+    layers = [Layer(wl, fmt, kind, args.rotate, W, torch) for wl in wls]
+
+    ms_step, tq_ms, gm_ms = run_layer_steps(layers, W, torch, args.steps, args.warmup, args.rotate)
+
+    flops = sum(L.gemm_flops() for L in layers)
+    tq_bytes = sum(L.tq_bytes() for L in layers)
+    tq_flops = sum(L.tq_flops() for L in layers)
+    tq_t = sum(tq_ms) / 1e3
+    gm_t = sum(gm_ms) / 1e3
+    gemm_peak = {"mxfp4": MXFP4_TFLOPS, "nvfp4": BF16_TFLOPS, "int4": INT8_TOPS}[fmt]
+    gemm_achieved = flops / gm_t / 1e12
+    tq_alu = tq_flops / tq_t / 1e12
+    tq_gbps = tq_bytes / tq_t / 1e9
+    x_dtype = wls[0].dtype
+    # dominant kernel by measured time
+    dom_gemm = gm_t >= tq_t
+    roof_gemm = {"kernel": "wush_w4a4_gemm", "bound": "mfma", "achieved": round(gemm_achieved, 2),
+                 "peak": gemm_peak, "unit": "TFLOP/s", "frac": round(gemm_achieved / gemm_peak, 4),
+                 "traffic": None, "avg_us": round(gm_t * 1e6 / len(layers), 2)}
+    t_alu = tq_flops / (VALU_FP32_TFLOPS * 1e12)
+    t_hbm = tq_bytes / (HBM_GBPS * 1e9)
+    if t_alu > t_hbm:
+        roof_tq = {"kernel": "wush_transform_quant", "bound": "alu", "achieved": round(tq_alu, 2),
+                   "peak": round(VALU_FP32_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(tq_alu / VALU_FP32_TFLOPS, 4),
+                   "traffic": None, "avg_us": round(tq_t * 1e6 / len(layers), 2),
+                   "hbm_GBps": round(tq_gbps, 1), "hbm_frac": round(tq_gbps / HBM_GBPS, 4)}
+    else:
+        roof_tq = {"kernel": "wush_transform_quant", "bound": "hbm", "achieved": round(tq_gbps, 1),
+                   "peak": HBM_GBPS, "unit": "GB/s", "frac": round(tq_gbps / HBM_GBPS, 4), "traffic": None,
+                   "avg_us": round(tq_t * 1e6 / len(layers), 2)}
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": fmt,
+        "data": "synthetic",
+        "config": {"workload": "+".join(L.wl.name for L in layers), "transform": kind, "format": fmt,
+                   "x_dtype": x_dtype, "tokens": layers[0].M,
+                   "layers": [[L.K, L.N] for L in layers], "rotate_buffers": args.rotate},
+        "quant_GBps": round(tq_gbps, 1),
+        "tq_us": round(tq_t * 1e6, 2),
+        "gemm_us": round(gm_t * 1e6, 2),
+        "roofline": roof_gemm if dom_gemm else roof_tq,
+        "tq_roofline": roof_tq,
+        "gemm_roofline": roof_gemm,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_had256(args, W, torch):
+    from synth.gen import CONFIGS, make_weights, bf16_bits, bf16_round
+    wl = CONFIGS["had256"]
+    B = args.batch
+    Wt = make_weights(wl)
+    d_out, d_in = Wt.shape
+    dev = "cuda"
+    planes = torch.empty((d_out, d_in // 256, 96), dtype=torch.uint8, device=dev)
+    sc = torch.empty((d_out, d_in // 256), dtype=torch.int16, device=dev)
+    W.wush_had256_pack_weights(torch.from_numpy(Wt).to(dev), planes, sc)
+    x = bf16_round(np.random.default_rng([5, 1]).standard_normal((B, d_in)).astype(np.float32))
+    xd = torch.from_numpy(bf16_bits(x).view(np.int16)).to(dev)
+    P = [planes] + [planes.clone() for _ in range(args.rotate - 1)]
+    S = [sc] + [sc.clone() for _ in range(args.rotate - 1)]
+    y = torch.empty((B, d_out), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        W.wush_had256_gemv(xd, P[i % args.rotate], S[i % args.rotate], y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        W.wush_had256_gemv(xd, P[i % args.rotate], S[i % args.rotate], y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    wbytes = d_out * (d_in // 256) * 98
+    byts = wbytes + B * d_in * 2 + B * d_out * 4
+    gbps = byts / (ms / 1e3) / 1e9
+    flops = 2.0 * B * d_out * d_in
+    out = {"metric": "Hadamard-256 3-bit GEMV weight stream GB/s", "value": round(gbps, 1), "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int3+fp32",
+           "data": "synthetic",
+           "config": {"workload": wl.name, "batch": B, "d_in": d_in, "d_out": d_out},
+           "tflops": round(flops / (ms / 1e3) / 1e12, 3),
+           "roofline": {"kernel": "wush_had256_gemv", "bound": "hbm", "achieved": round(gbps, 1),
+                        "peak": HBM_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_GBPS, 4), "traffic": None,
+                        "avg_us": round(ms * 1e3, 2)}}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

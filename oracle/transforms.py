@@ -56,16 +56,16 @@ def weight_moments(Wt, bs):
     """A_b = W_b W_b^T in fp64 for every block.  Wt is [d_out][d_in] (nn.Linear)."""
     Wt = np.asarray(Wt, dtype=np.float64)
     d_out, d_in = Wt.shape
-    Wb = Wt.reshape(d_out, d_in // bs, bs)            # [o][b][i]
-    return np.einsum("obi,obj->bij", Wb, Wb)
+    Wb = Wt.reshape(d_out, d_in // bs, bs).transpose(1, 2, 0)   # [b][i][o]
+    return Wb @ Wb.transpose(0, 2, 1)
 
 
 def activation_moments(Xt, bs):
     """B_b = X_b X_b^T / n in fp64 for every block.  Xt is [n][d_in] (token-major)."""
     Xt = np.asarray(Xt, dtype=np.float64)
     n, d_in = Xt.shape
-    Xb = Xt.reshape(n, d_in // bs, bs)
-    return np.einsum("tbi,tbj->bij", Xb, Xb) / n
+    Xb = Xt.reshape(n, d_in // bs, bs).transpose(1, 2, 0)       # [b][i][t]
+    return (Xb @ Xb.transpose(0, 2, 1)) / n
 
 
 def cholesky_damped(A):

@@ -131,7 +131,11 @@ def test_pack_weights_bit_exact(fmt, kind):
         assert np.float32(gg) == g
 
 
-GEMM_SHAPES = [(16, 16, 128), (128, 256, 256), (100, 70, 384), (257, 129, 640), (64, 512, 1024)]
+# K % 256 == 0 runs the LDS-staged 256x256 kernel (ragged M / N included);
+# other K (multiples of 128) the direct-load kernel
+GEMM_SHAPES = [(16, 16, 128), (100, 70, 384), (257, 129, 640),
+               (128, 256, 256), (64, 512, 1024), (300, 520, 512), (17, 300, 768),
+               (1000, 260, 2048), (512, 1024, 4096)]
 
 
 def _rand_operands(fmt, M, N, K, seed):
