@@ -159,20 +159,33 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_direct(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged kernel (K % 256 == 0).
+// LDS-staged kernel (any K % 128 == 0).
 //
-// Workgroup tile 256 x 256, four waves of 128 x 128 each (2 x 2), so every
-// wave issues 64 MFMAs per 16 fragment reads from LDS: 16 bytes per clock per
-// wave, well inside the LDS bandwidth.  The 256 accumulator registers per
-// lane live in AGPRs; occupancy is one wave per SIMD.
+// Workgroup tile 256 x 256, four waves of 128 x 128 each (2 x 2): per K step
+// of 256 a wave reads 32 fragments (32 KB) from LDS and issues 128 MFMAs, so
+// LDS reads stay at 16 bytes per clock per wave.  The 256 accumulator
+// registers per lane live in AGPRs; occupancy is one wave per SIMD.
 //
-// Staging: one K step of 256 moves 256 rows x 128 bytes of each operand.
-// Each 1 KB fragment (16 rows x 128 K values of one MFMA sub-step) is brought
-// from global memory straight into LDS with global_load_lds_dwordx4, lane l
-// landing at byte 16 l of the fragment, which is exactly where the consuming
-// MFMA lane l reads it back with one ds_read_b128: both sides are
-// lane-linear, so there are no bank conflicts.  Two stages (128 KB) are
-// double-buffered; stage ks+1 is loaded while stage ks feeds the MFMAs.
+// Global -> LDS: one K step moves 256 rows x 128 bytes of each operand.  Each
+// buffer_load_dwordx4 covers 8 rows x one full 128-byte line (8 lanes per row),
+// so every L2 request is a whole line; the data lands in VGPRs one step ahead
+// of use and is then written to LDS with ds_write_b128.  (Measured on MI355X:
+// 16-byte-per-lane LDS DMA of the same bytes keeps the texture address unit
+// saturated and runs ~1.5x slower, and 64-byte row pieces halve the request
+// size again.)
+//
+// LDS layout: a 16-row x 128-byte block per row group (both MFMA sub-steps of
+// the step), 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7).  Both
+// the writes (8 lanes per row) and the MFMA reads (16 rows, one chunk each, per
+// 16-lane phase) then touch 16 distinct 4-bank groups: no bank conflicts.
+// E8M0 scales (8 per row per step: 4 per MFMA sub-step) are stored as
+// [rr][sub-step][16 rows][4 bytes] with a 144-byte pitch per lane row rr (another
+// conflict-free spread), so a lane finds the sub-step scales of its 8 rows in
+// 32 contiguous bytes.
+//
+// The two LDS stages are distinct __shared__ arrays and the K loop is unrolled
+// by two, so every access names its array statically and the compiler knows
+// that writing the next stage does not alias reading the current one.
 //
 // Tile order: workgroups are dealt to the 8 XCDs round-robin (id % 8), so the
 // tile index is remapped to give each XCD a contiguous run of tiles, walked in
@@ -180,13 +193,21 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_direct(const uint8_t* __restri
 // in their own L2.
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kFragBytes = 2 * 16 * 2 * 1024;    // operands x row groups x sub-steps x fragment
-constexpr int kScaleBytes = 2 * 256 * 8;          // operands x rows x 8 scale bytes of one K step
-constexpr int kStageBytes = kFragBytes + kScaleBytes;
+constexpr int kFragStage = 2 * 16 * 2048;        // operands x row groups x (16 rows x 128 B)
+constexpr int kScalePitch = 144;                 // bytes per lane row rr in the scale area
+constexpr int kScaleOp = 16 * kScalePitch;       // one operand's scales for one step
+constexpr int kStageBytes = kFragStage + 2 * kScaleOp;
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
+
+template <int S>
+__device__ __forceinline__ uint8_t* stage_buf() {
+  if constexpr (S == 0) return g_stage0;
+  else return g_stage1;
+}
 
 // Buffer descriptor over `bytes` bytes at `base` (raw, unswizzled; dword 3 =
 // 0x00020000 selects 32-bit data format for untyped buffer access on CDNA).
@@ -195,21 +216,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-// 16 bytes per lane from (voffset + soffset) straight into LDS at
-// lds_frag + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the LDS base).
-// The instruction's immediate offset would move the LDS destination as well,
-// so any uniform displacement goes into soffset instead.
-__device__ __forceinline__ void load_frag_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_frag) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds_frag), 16, voff, soff, 0, 0);
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
-// 4 bytes per lane into LDS at lds_dst + 4 * lane.
-__device__ __forceinline__ void load_dword_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds_dst), 4, voff, soff, 0, 0);
-}
-
-__device__ __forceinline__ uint4 read_frag(const uint8_t* lds_frag, int lane) {
-  return *reinterpret_cast<const uint4*>(lds_frag + lane * 16);
+// Workgroup barrier without the release/acquire fence of __syncthreads(): that
+// fence would also wait for the next stage's global loads.  LDS needs no cache
+// maintenance; waiting for this wave's own LDS traffic first (lgkmcnt(0))
+// orders its writes before, and its reads of a buffer before the rewrite of it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -226,66 +245,143 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& t
   tn = in_group / gsize;
 }
 
+struct Staging {
+  uint4 a[8], b[8];   // 8 rows x 128 B per instruction, this wave's 64 rows of A and of B
+  uint2 s[2];         // 64 rows x 8 scale bytes per instruction, operand (wave >> 1)
+};
+
+struct GemmCtx {
+  __amdgpu_buffer_rsrc_t ra, rb, rs;
+  uint32_t a_off, b_off;   // loader row r0 = 64 wave + lane / 8, chunk lane % 8
+  uint32_t s_off[2];       // loader scale rows (wave & 1) 128 + 64 u + lane
+  uint32_t w_frag;         // LDS byte offset of this lane's chunk within a 16-row block (instruction u even)
+  uint32_t w_frag1;        // same for odd u (rows 8..15 of the block)
+  uint32_t w_scale[2];     // LDS byte offset of this lane's scale row (per u)
+  uint32_t r_frag[2];      // LDS byte offset of this lane's read chunk, per sub-step j
+  uint32_t r_scale_a, r_scale_b;
+  int wave, lane, wm, wn, nks;
+  bool half_tail;              // K % 256 == 128: the last step has one MFMA sub-step
+  uint32_t a_step8, b_step8;   // byte distance of 8 rows in A / B (8 * K / 2)
+};
+
+__device__ __forceinline__ void load_stage(const GemmCtx& c, int k, Staging& g) {
+  const uint32_t kb = static_cast<uint32_t>(k) * 128;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    g.a[u] = load16(c.ra, c.a_off + u * c.a_step8, kb);
+    g.b[u] = load16(c.rb, c.b_off + u * c.b_step8, kb);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) g.s[u] = load8(c.rs, c.s_off[u], static_cast<uint32_t>(k) * 8);
+}
+
+template <int S>
+__device__ __forceinline__ void store_stage(const GemmCtx& c, const Staging& g) {
+  uint8_t* st = stage_buf<S>();
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    // instruction u covers rows 64 wave + 8 u .. of the tile = row group 4 wave + u / 2
+    const uint32_t blk = (4 * c.wave + u / 2) * 2048 + ((u & 1) ? c.w_frag1 : c.w_frag);
+    *reinterpret_cast<uint4*>(st + blk) = g.a[u];
+    *reinterpret_cast<uint4*>(st + 16 * 2048 + blk) = g.b[u];
+  }
+  uint8_t* ss = st + kFragStage + (c.wave >> 1) * kScaleOp;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    *reinterpret_cast<uint32_t*>(ss + c.w_scale[u]) = g.s[u].x;        // sub-step 0 scales of the row
+    *reinterpret_cast<uint32_t*>(ss + c.w_scale[u] + 64) = g.s[u].y;   // sub-step 1
+  }
+}
+
+// One K step (256) on stage S: read its fragments and scales, refill the other
+// stage from the staging registers, start the global loads two steps ahead,
+// then the 128 MFMAs.
+template <int S>
+__device__ __forceinline__ void k_step(const GemmCtx& c, int k, Staging& g, v4f (&acc)[8][8]) {
+  stage_barrier();
+  const uint8_t* st = stage_buf<S>();
+  const uint32_t sh = 8u * static_cast<uint32_t>(c.lane >> 4);   // this lane's K group within the sub-step
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j == 1 && c.half_tail && k == c.nks - 1) break;   // uniform: K ends half way
+    __builtin_amdgcn_sched_barrier(0);
+    // 8 rows x 4 scale bytes of sub-step j for A (rows of this wave's 8 A fragments) and B
+    const uint4* spa = reinterpret_cast<const uint4*>(st + kFragStage + c.r_scale_a + 64 * j);
+    const uint4* spb = reinterpret_cast<const uint4*>(st + kFragStage + kScaleOp + c.r_scale_b + 64 * j);
+    const uint4 a0 = spa[0], a1 = spa[1], b0 = spb[0], b1 = spb[1];
+    uint4 af[8], bf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bf[i] = *reinterpret_cast<const uint4*>(st + (16 + c.wn * 8 + i) * 2048 + c.r_frag[j]);
+      af[i] = *reinterpret_cast<const uint4*>(st + (c.wm * 8 + i) * 2048 + c.r_frag[j]);
+    }
+    if (j == 0) {
+      // refill the other stage from the staging registers, then start the
+      // global loads two steps ahead into them.  Unconditional (clamped to the
+      // last step; the surplus is never read): a conditional refill would make
+      // the compiler keep two copies of the staging registers alive.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      store_stage<S ^ 1>(c, g);
+      load_stage(c, min(k + 2, c.nks - 1), g);
+    }
+    const uint32_t sa[8] = {a0.x >> sh, a0.y >> sh, a0.z >> sh, a0.w >> sh, a1.x >> sh, a1.y >> sh, a1.z >> sh, a1.w >> sh};
+    const uint32_t sb[8] = {b0.x >> sh, b0.y >> sh, b0.z >> sh, b0.w >> sh, b1.x >> sh, b1.y >> sh, b1.z >> sh, b1.w >> sh};
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i][q] = mfma_fp4<0>(bf[i], sb[i], af[q], sa[q], acc[i][q]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
                                                         const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
                                                         float* __restrict__ Y, int M, int N, int K) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  GemmCtx c;
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.wm = c.wave >> 1;
+  c.wn = c.wave & 1;
+  c.nks = (K + 255) / 256;
+  c.half_tail = (K & 255) != 0;
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
-  const int rr = lane & 15, grp = lane >> 4;
-
-  // 32-bit per-lane byte offsets from the uniform base pointers (the host checks
-  // that every operand is below 2^31 bytes), so loads use scalar-base addressing.
-  // loader: this wave stages row groups 4*wave .. 4*wave+3 of both operands
+  const int rr = c.lane & 15, grp = c.lane >> 4;
+  // 32-bit byte offsets from uniform bases (the host checks every operand is
+  // below 2^31 bytes).  Rows past the edge read the last row (never stored).
+  // A K of 128 (mod 256) leaves a half step: its upper 64 bytes per row (and 4
+  // scale bytes) read past the row, the next row or zeros from the bounded
+  // descriptor, and feed only the sub-step that the last step skips.
   const uint32_t krow = static_cast<uint32_t>(K) / 2, srow = static_cast<uint32_t>(K) / 32;
-  uint32_t a_off[4], b_off[4];
+  const int lr = c.lane >> 3, lc = c.lane & 7;
+  const int ra = min(m0 + 64 * c.wave + lr, M - 1), rb = min(n0 + 64 * c.wave + lr, N - 1);
+  c.a_off = static_cast<uint32_t>(ra) * krow + lc * 16;
+  c.b_off = static_cast<uint32_t>(rb) * krow + lc * 16;
+  c.a_step8 = 8 * krow;
+  c.b_step8 = 8 * krow;
+  const int s_op = c.wave >> 1;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int ra = min(m0 + (4 * wave + t) * 16 + rr, M - 1);
-    const int rb = min(n0 + (4 * wave + t) * 16 + rr, N - 1);
-    a_off[t] = static_cast<uint32_t>(ra) * krow + grp * 32;
-    b_off[t] = static_cast<uint32_t>(rb) * krow + grp * 32;
+  for (int u = 0; u < 2; ++u) {
+    const int row = (c.wave & 1) * 128 + 64 * u + c.lane;            // row within the tile
+    const int base = s_op ? n0 : m0, lim = s_op ? N - 1 : M - 1;
+    c.s_off[u] = static_cast<uint32_t>(min(base + row, lim)) * srow;
+    // scale position: lane row rr' = row % 16, then [sub-step][half = row / 128][i = (row / 16) % 8]
+    c.w_scale[u] = (row & 15) * kScalePitch + ((row >> 7) * 8 + ((row >> 4) & 7)) * 4;
   }
-  // scales: this wave stages 128 rows (half (wave & 1)) of one operand's 8 scale
-  // bytes per K step; one LDS DMA moves 64 lanes x 4 bytes = 32 rows, lane l
-  // fetching half (l % 2) of row 32 c + l / 2, so four instructions per wave
-  const int s_op = wave >> 1;                         // 0: A scales, 1: B scales
-  uint32_t s_off[4];
+  // writer chunk position: row r = lr (+8 for odd u), logical chunk lc
+  c.w_frag = lr * 128 + ((lc ^ ((lr >> 1) & 7)) * 16);
+  c.w_frag1 = (lr + 8) * 128 + ((lc ^ (((lr + 8) >> 1) & 7)) * 16);
+  // reader: row rr, logical chunk 4 j + grp
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int row = (wave & 1) * 128 + c * 32 + (lane >> 1);
-    const int lim = s_op ? N - 1 : M - 1;
-    const int base = s_op ? n0 : m0;
-    s_off[c] = static_cast<uint32_t>(min(base + row, lim)) * srow + (lane & 1) * 4;
-  }
-  // consumer: wave (wm, wn) owns rows m0 + 128 wm .., cols n0 + 128 wn ..
-  const int wm = wave >> 1, wn = wave & 1;
-
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, static_cast<uint32_t>(M) * krow);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, static_cast<uint32_t>(N) * krow);
-  const __amdgpu_buffer_rsrc_t rs = s_op ? make_rsrc(SB, static_cast<uint32_t>(N) * srow)
-                                         : make_rsrc(SA, static_cast<uint32_t>(M) * srow);
-
-  auto issue_stage = [&](int ks, int buf) {
-    uint8_t* st = smem + buf * kStageBytes;
-    const uint32_t kb = static_cast<uint32_t>(ks) * 128;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int rg = 4 * wave + t;
-      load_frag_lds(ra, a_off[t], kb, st + ((0 * 16 + rg) * 2 + 0) * 1024);
-      load_frag_lds(ra, a_off[t], kb + 16, st + ((0 * 16 + rg) * 2 + 1) * 1024);
-      load_frag_lds(rb, b_off[t], kb, st + ((1 * 16 + rg) * 2 + 0) * 1024);
-      load_frag_lds(rb, b_off[t], kb + 16, st + ((1 * 16 + rg) * 2 + 1) * 1024);
-    }
-    // scale rows [row][8 bytes], A then B
-    uint8_t* ss = st + kFragBytes + s_op * 2048 + (wave & 1) * 1024;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) load_dword_lds(rs, s_off[c], static_cast<uint32_t>(ks) * 8, ss + c * 256);
-  };
+  for (int j = 0; j < 2; ++j) c.r_frag[j] = rr * 128 + ((((4 * j + grp) ^ ((rr >> 1) & 7))) * 16);
+  c.r_scale_a = rr * kScalePitch + c.wm * 32;
+  c.r_scale_b = rr * kScalePitch + c.wn * 32;
+  // descriptors bound the operands exactly (out-of-range lanes read zeros)
+  c.ra = make_rsrc(A, static_cast<uint32_t>(M) * krow);
+  c.rb = make_rsrc(B, static_cast<uint32_t>(N) * krow);
+  c.rs = s_op ? make_rsrc(SB, static_cast<uint32_t>(N) * srow) : make_rsrc(SA, static_cast<uint32_t>(M) * srow);
 
   v4f acc[8][8];
 #pragma unroll
@@ -293,57 +389,35 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restri
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[i][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int nks = K / 256;
-  issue_stage(0, 0);
+  Staging g;
+  load_stage(c, 0, g);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  store_stage<0>(c, g);
+  load_stage(c, min(1, c.nks - 1), g);
+  int k = 0;
 #pragma unroll 1
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // everything this step needs goes from LDS into registers before the next
-    // stage's LDS DMA is issued: an LDS read issued after an LDS DMA must wait
-    // for it (the compiler cannot tell the two stage buffers apart)
-    const uint8_t* st = smem + buf * kStageBytes;
-    uint4 af[2][8], bf[2][8];
-    uint32_t sa[8], sb[8];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        af[j][i] = read_frag(st + ((0 * 16 + wm * 8 + i) * 2 + j) * 1024, lane);
-        bf[j][i] = read_frag(st + ((1 * 16 + wn * 8 + i) * 2 + j) * 1024, lane);
-      }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sa[i] = *reinterpret_cast<const uint16_t*>(st + kFragBytes + (wm * 128 + i * 16 + rr) * 8 + grp * 2);
-      sb[i] = *reinterpret_cast<const uint16_t*>(st + kFragBytes + 2048 + (wn * 128 + i * 16 + rr) * 8 + grp * 2);
-    }
-    if (ks + 1 < nks) issue_stage(ks + 1, buf ^ 1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[i][q] = mfma_fp4<0>(bf[0][i], sb[i], af[0][q], sa[q], acc[i][q]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[i][q] = mfma_fp4<1>(bf[1][i], sb[i], af[1][q], sa[q], acc[i][q]);
+  for (; k + 1 < c.nks; k += 2) {
+    k_step<0>(c, k, g, acc);
+    k_step<1>(c, k + 1, g, acc);
   }
+  if (k < c.nks) k_step<0>(c, k, g, acc);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // surplus staging loads
 
   // lane holds Y[m0 + 128 wm + 16 q + rr][n0 + 128 wn + 16 i + 4 grp + 0..3]
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int m = m0 + wm * 128 + q * 16 + rr;
+    const int m = m0 + c.wm * 128 + q * 16 + rr;
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int n = n0 + wn * 128 + i * 16 + 4 * grp;
+      const int n = n0 + c.wn * 128 + i * 16 + 4 * grp;
       float* dst = Y + static_cast<size_t>(m) * N + n;
       if (n + 3 < N && (N & 3) == 0) {
         *reinterpret_cast<float4*>(dst) = make_float4(acc[i][q][0], acc[i][q][1], acc[i][q][2], acc[i][q][3]);
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (n + c < N) dst[c] = acc[i][q][c];
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) dst[e] = acc[i][q][e];
       }
     }
   }
@@ -355,7 +429,8 @@ namespace wush {
 
 wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
                        float* Y, hipStream_t stream) {
-  if (K % 256 == 0) {
+  const bool small = static_cast<long>(M) * (K / 2) < (1L << 31) && static_cast<long>(N) * (K / 2) < (1L << 31);
+  if (small) {
     const long tiles = static_cast<long>((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     if (tiles > 0x7fffffffL) return fail(WUSH_E_SHAPE, "wush_w4a4_gemm: too many tiles");
     hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, SA, B, SB, Y, M,

@@ -131,11 +131,11 @@ def test_pack_weights_bit_exact(fmt, kind):
         assert np.float32(gg) == g
 
 
-# K % 256 == 0 runs the LDS-staged 256x256 kernel (ragged M / N included);
-# other K (multiples of 128) the direct-load kernel
-GEMM_SHAPES = [(16, 16, 128), (100, 70, 384), (257, 129, 640),
-               (128, 256, 256), (64, 512, 1024), (300, 520, 512), (17, 300, 768),
-               (1000, 260, 2048), (512, 1024, 4096)]
+# the LDS-staged kernel handles every K % 128 == 0; K / 128 steps cover the
+# pipeline's cases (1, 2, 3 steps; whole groups of 4; groups plus 1-3 extra)
+GEMM_SHAPES = [(16, 16, 128), (100, 70, 384), (257, 129, 640), (128, 256, 256), (64, 512, 1024),
+               (300, 520, 512), (17, 300, 768), (1000, 260, 2048), (512, 1024, 4096), (260, 513, 1152),
+               (33, 800, 1408)]
 
 
 def _rand_operands(fmt, M, N, K, seed):
