@@ -159,33 +159,37 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_direct(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged kernel (any K % 128 == 0).
+// LDS-staged, software-pipelined kernel (K >= 256, K % 128 == 0).
 //
-// Workgroup tile 256 x 256, four waves of 128 x 128 each (2 x 2): per K step
-// of 256 a wave reads 32 fragments (32 KB) from LDS and issues 128 MFMAs, so
-// LDS reads stay at 16 bytes per clock per wave.  The 256 accumulator
-// registers per lane live in AGPRs; occupancy is one wave per SIMD.
+// Workgroup tile 256 x 256, four waves of 128 x 128 each (2 x 2); the 256
+// accumulator registers per lane live in AGPRs (one wave per SIMD).  K is
+// staged through LDS in blocks of 256 and consumed in sub-steps of 128: per
+// sub-step ("phase") a wave issues 64 MFMAs and reads 16 fragments (16 KB).
 //
-// Global -> LDS: one K step moves 256 rows x 128 bytes of each operand.  Each
-// buffer_load_dwordx4 covers 8 rows x one full 128-byte line (8 lanes per row),
-// so every L2 request is a whole line; the data lands in VGPRs one step ahead
-// of use and is then written to LDS with ds_write_b128.  (Measured on MI355X:
-// 16-byte-per-lane LDS DMA of the same bytes keeps the texture address unit
-// saturated and runs ~1.5x slower, and 64-byte row pieces halve the request
-// size again.)
+// Pipeline, per phase p = 2 k + j (block k, sub-step j), overlapped with the
+// MFMAs of p, which take their operands from registers:
+//   * LDS reads of sub-step p+1 into the other fragment register set (the A
+//     fragments one by one, each right after the MFMAs that free its
+//     registers),
+//   * j = 0: LDS writes of block k+1's B operand from its staging registers,
+//     then the global loads of block k+2's B into them;
+//     j = 1: the same for A, blocks k+2 and k+3,
+// then one workgroup barrier.  Two LDS block buffers (68 KB each); every
+// global load has two phases to land, and a buffer is rewritten only after the
+// barrier that follows its last read.
 //
-// LDS layout: a 16-row x 128-byte block per row group (both MFMA sub-steps of
-// the step), 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7).  Both
-// the writes (8 lanes per row) and the MFMA reads (16 rows, one chunk each, per
-// 16-lane phase) then touch 16 distinct 4-bank groups: no bank conflicts.
-// E8M0 scales (8 per row per step: 4 per MFMA sub-step) are stored as
-// [rr][sub-step][16 rows][4 bytes] with a 144-byte pitch per lane row rr (another
-// conflict-free spread), so a lane finds the sub-step scales of its 8 rows in
-// 32 contiguous bytes.
-//
-// The two LDS stages are distinct __shared__ arrays and the K loop is unrolled
-// by two, so every access names its array statically and the compiler knows
-// that writing the next stage does not alias reading the current one.
+// Global -> registers: buffer_load_dwordx4 with lane (lr, lc) = (lane / 8,
+// lane % 8) fetching the 16-byte chunk lc of row lr: 8 full 128-byte rows
+// (one block of one row) per instruction.
+// LDS layout of a 2 KB fragment pair (16 rows x 128 B, both sub-steps): chunk
+// c of row r at 16-byte slot 8 r + (c ^ ((r >> 1) & 7)); a ds_write_b128
+// (16 lanes: two rows) and a ds_read_b128 (16 lanes: rows 0..15 of one chunk)
+// both touch all 64 banks once.
+// E8M0 scales, one byte each, as plane [sub-step j][K group g] of
+// [lane row rr][8 half + i] for tile row 128 half + 16 i + rr: a lane reads
+// the 8 scale bytes of its 8 fragments with one ds_read_b64 and the MFMA's
+// op_sel picks the byte.  The loaders write the planes byte by byte, with the
+// rows of one instruction chosen so that its 64 lanes hit 64 distinct dwords.
 //
 // Tile order: workgroups are dealt to the 8 XCDs round-robin (id % 8), so the
 // tile index is remapped to give each XCD a contiguous run of tiles, walked in
@@ -193,29 +197,17 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_direct(const uint8_t* __restri
 // in their own L2.
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kFragStage = 2 * 16 * 2048;        // operands x row groups x (16 rows x 128 B)
-constexpr int kScalePitch = 144;                 // bytes per lane row rr in the scale area
-constexpr int kScaleOp = 16 * kScalePitch;       // one operand's scales for one step
-constexpr int kStageBytes = kFragStage + 2 * kScaleOp;
+constexpr int kFragOp = 16 * 2048;                 // one operand of one block: 16 fragment pairs
+constexpr int kScaleOp = 8 * 256;                  // one operand's scale planes
+constexpr int kStageBytes = 2 * kFragOp + 2 * kScaleOp;
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
 
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
-
-template <int S>
-__device__ __forceinline__ uint8_t* stage_buf() {
-  if constexpr (S == 0) return g_stage0;
-  else return g_stage1;
-}
-
-// Buffer descriptor over `bytes` bytes at `base` (raw, unswizzled; dword 3 =
-// 0x00020000 selects 32-bit data format for untyped buffer access on CDNA).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw, unswizzled; dword 3 = 0x00020000 selects 32-bit data format for untyped access on CDNA
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
                                            0x00020000);
 }
-
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
@@ -223,12 +215,21 @@ __device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
-// Workgroup barrier without the release/acquire fence of __syncthreads(): that
-// fence would also wait for the next stage's global loads.  LDS needs no cache
-// maintenance; waiting for this wave's own LDS traffic first (lgkmcnt(0))
-// orders its writes before, and its reads of a buffer before the rewrite of it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// s_waitcnt immediates (gfx9 layout: vmcnt [3:0] + [15:14], expcnt [6:4],
+// lgkmcnt [11:8]); issued through the builtin so that the compiler's own wait
+// insertion knows which loads have completed.
+constexpr unsigned kWaitLgkm0 = 0xC07F;   // lgkmcnt(0)
+constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0)
+
+// All of this wave's LDS traffic done, then the workgroup barrier.  No memory
+// fence (that of __syncthreads() would also wait for the in-flight global
+// loads): only LDS is shared, and lgkmcnt(0) orders this wave's writes before,
+// and its reads of a buffer before any rewrite of it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -245,143 +246,178 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& t
   tn = in_group / gsize;
 }
 
-struct Staging {
-  uint4 a[8], b[8];   // 8 rows x 128 B per instruction, this wave's 64 rows of A and of B
-  uint2 s[2];         // 64 rows x 8 scale bytes per instruction, operand (wave >> 1)
-};
+struct Frags { uint4 a[8], b[8]; uint2 sa, sb; };   // sa / sb: 8 scale bytes, fragment i in byte i
+struct Stage { uint4 d[8]; uint2 s; };                // one operand of one block: this wave's 64 rows + 64 scale rows
 
 struct GemmCtx {
-  __amdgpu_buffer_rsrc_t ra, rb, rs;
-  uint32_t a_off, b_off;   // loader row r0 = 64 wave + lane / 8, chunk lane % 8
-  uint32_t s_off[2];       // loader scale rows (wave & 1) 128 + 64 u + lane
-  uint32_t w_frag;         // LDS byte offset of this lane's chunk within a 16-row block (instruction u even)
-  uint32_t w_frag1;        // same for odd u (rows 8..15 of the block)
-  uint32_t w_scale[2];     // LDS byte offset of this lane's scale row (per u)
-  uint32_t r_frag[2];      // LDS byte offset of this lane's read chunk, per sub-step j
-  uint32_t r_scale_a, r_scale_b;
-  int wave, lane, wm, wn, nks;
-  bool half_tail;              // K % 256 == 128: the last step has one MFMA sub-step
-  uint32_t a_step8, b_step8;   // byte distance of 8 rows in A / B (8 * K / 2)
+  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+  uint32_t a_off, b_off;         // loader: row 64 wave + lane / 8, chunk lane % 8 (+ u * row_step8 for instruction u)
+  uint32_t row_step8;            // bytes of 8 rows
+  uint32_t sa_off, sb_off;       // loader: this lane's scale row (see kernel)
+  uint32_t w_frag0, w_frag1;     // LDS slot of the loader's chunk within a fragment pair (even / odd u)
+  uint32_t w_scale;              // LDS offset of the loader's scale byte within plane 0
+  uint32_t r_frag[2];            // LDS slot of this lane's read chunk within a fragment pair, per sub-step
+  uint32_t r_scale_a, r_scale_b; // LDS offset of this lane's 8 scale bytes within plane (0, g)
+  int wave, wm, wn, nb;
 };
 
-__device__ __forceinline__ void load_stage(const GemmCtx& c, int k, Staging& g) {
-  const uint32_t kb = static_cast<uint32_t>(k) * 128;
+__device__ __forceinline__ void load_op(__amdgpu_buffer_rsrc_t rd, uint32_t d_off, __amdgpu_buffer_rsrc_t rs,
+                                        uint32_t s_off, uint32_t step8, int k, Stage& g) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    g.a[u] = load16(c.ra, c.a_off + u * c.a_step8, kb);
-    g.b[u] = load16(c.rb, c.b_off + u * c.b_step8, kb);
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) g.s[u] = load8(c.rs, c.s_off[u], static_cast<uint32_t>(k) * 8);
+  for (int u = 0; u < 8; ++u) g.d[u] = load16(rd, d_off + u * step8, static_cast<uint32_t>(k) * 128);
+  g.s = load8(rs, s_off, static_cast<uint32_t>(k) * 8);
 }
 
-template <int S>
-__device__ __forceinline__ void store_stage(const GemmCtx& c, const Staging& g) {
-  uint8_t* st = stage_buf<S>();
+// one operand (op 0 = A, 1 = B) of a block into the LDS buffer `buf`
+__device__ __forceinline__ void write_op(const GemmCtx& c, uint8_t* buf, int op, const Stage& g) {
+  uint8_t* fb = buf + op * kFragOp + c.wave * (4 * 2048);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    // instruction u covers rows 64 wave + 8 u .. of the tile = row group 4 wave + u / 2
-    const uint32_t blk = (4 * c.wave + u / 2) * 2048 + ((u & 1) ? c.w_frag1 : c.w_frag);
-    *reinterpret_cast<uint4*>(st + blk) = g.a[u];
-    *reinterpret_cast<uint4*>(st + 16 * 2048 + blk) = g.b[u];
-  }
-  uint8_t* ss = st + kFragStage + (c.wave >> 1) * kScaleOp;
+  for (int u = 0; u < 8; ++u)
+    *reinterpret_cast<uint4*>(fb + (u >> 1) * 2048 + ((u & 1) ? c.w_frag1 : c.w_frag0)) = g.d[u];
+  uint8_t* sp = buf + 2 * kFragOp + op * kScaleOp + c.w_scale;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    *reinterpret_cast<uint32_t*>(ss + c.w_scale[u]) = g.s[u].x;        // sub-step 0 scales of the row
-    *reinterpret_cast<uint32_t*>(ss + c.w_scale[u] + 64) = g.s[u].y;   // sub-step 1
+  for (int b = 0; b < 4; ++b) {
+    sp[b * 256] = static_cast<uint8_t>(g.s.x >> (8 * b));          // sub-step 0, K group b
+    sp[(4 + b) * 256] = static_cast<uint8_t>(g.s.y >> (8 * b));    // sub-step 1, K group b
   }
 }
 
-// One K step (256) on stage S: read its fragments and scales, refill the other
-// stage from the staging registers, start the global loads two steps ahead,
-// then the 128 MFMAs.
-template <int S>
-__device__ __forceinline__ void k_step(const GemmCtx& c, int k, Staging& g, v4f (&acc)[8][8]) {
-  stage_barrier();
-  const uint8_t* st = stage_buf<S>();
-  const uint32_t sh = 8u * static_cast<uint32_t>(c.lane >> 4);   // this lane's K group within the sub-step
+__device__ __forceinline__ uint4 read_a(const GemmCtx& c, const uint8_t* buf, int j, int q) {
+  return *reinterpret_cast<const uint4*>(buf + (c.wm * 8 + q) * 2048 + c.r_frag[j]);
+}
+
+// B fragments and both operands' scales of sub-step j of the block in `buf`
+__device__ __forceinline__ void read_b_scales(const GemmCtx& c, const uint8_t* buf, int j, Frags& f) {
+  f.sa = *reinterpret_cast<const uint2*>(buf + 2 * kFragOp + j * 1024 + c.r_scale_a);
+  f.sb = *reinterpret_cast<const uint2*>(buf + 2 * kFragOp + kScaleOp + j * 1024 + c.r_scale_b);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (j == 1 && c.half_tail && k == c.nks - 1) break;   // uniform: K ends half way
-    __builtin_amdgcn_sched_barrier(0);
-    // 8 rows x 4 scale bytes of sub-step j for A (rows of this wave's 8 A fragments) and B
-    const uint4* spa = reinterpret_cast<const uint4*>(st + kFragStage + c.r_scale_a + 64 * j);
-    const uint4* spb = reinterpret_cast<const uint4*>(st + kFragStage + kScaleOp + c.r_scale_b + 64 * j);
-    const uint4 a0 = spa[0], a1 = spa[1], b0 = spb[0], b1 = spb[1];
-    uint4 af[8], bf[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      bf[i] = *reinterpret_cast<const uint4*>(st + (16 + c.wn * 8 + i) * 2048 + c.r_frag[j]);
-      af[i] = *reinterpret_cast<const uint4*>(st + (c.wm * 8 + i) * 2048 + c.r_frag[j]);
-    }
-    if (j == 0) {
-      // refill the other stage from the staging registers, then start the
-      // global loads two steps ahead into them.  Unconditional (clamped to the
-      // last step; the surplus is never read): a conditional refill would make
-      // the compiler keep two copies of the staging registers alive.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      store_stage<S ^ 1>(c, g);
-      load_stage(c, min(k + 2, c.nks - 1), g);
-    }
-    const uint32_t sa[8] = {a0.x >> sh, a0.y >> sh, a0.z >> sh, a0.w >> sh, a1.x >> sh, a1.y >> sh, a1.z >> sh, a1.w >> sh};
-    const uint32_t sb[8] = {b0.x >> sh, b0.y >> sh, b0.z >> sh, b0.w >> sh, b1.x >> sh, b1.y >> sh, b1.z >> sh, b1.w >> sh};
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][q] = mfma_fp4<0>(bf[i], sb[i], af[q], sa[q], acc[i][q]);
-  }
+  for (int i = 0; i < 8; ++i)
+    f.b[i] = *reinterpret_cast<const uint4*>(buf + kFragOp + (c.wn * 8 + i) * 2048 + c.r_frag[j]);
+}
+
+// MFMA for B fragment I and A fragment Q: scale bytes I and Q sit in byte I % 4
+// (resp. Q % 4) of dword I / 4 (Q / 4).
+template <int I, int Q>
+__device__ __forceinline__ void mfma_iq(const Frags& f, v4f& acc) {
+  const uint32_t sb = (I < 4) ? f.sb.x : f.sb.y;
+  const uint32_t sa = (Q < 4) ? f.sa.x : f.sa.y;
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as_operand(f.b[I]), as_operand(f.a[Q]), acc, 4, 4, I % 4,
+                                                         static_cast<int>(sb), Q % 4, static_cast<int>(sa));
+}
+
+template <int Q>
+__device__ __forceinline__ void mfma_column(const Frags& f, v4f (&acc)[8][8]) {
+  mfma_iq<0, Q>(f, acc[0][Q]);
+  mfma_iq<1, Q>(f, acc[1][Q]);
+  mfma_iq<2, Q>(f, acc[2][Q]);
+  mfma_iq<3, Q>(f, acc[3][Q]);
+  mfma_iq<4, Q>(f, acc[4][Q]);
+  mfma_iq<5, Q>(f, acc[5][Q]);
+  mfma_iq<6, Q>(f, acc[6][Q]);
+  mfma_iq<7, Q>(f, acc[7][Q]);
+}
+
+// Slot Q of a phase: the 8 MFMAs of column Q of the current sub-step on
+// `cur`, interleaved with this slot's share of the memory work so that no
+// unit sees a burst: B fragment Q of the next sub-step into `nxt`, staging
+// register Q written to LDS and reloaded from the next block of its operand,
+// scale plane Q written, and at the end A fragment Q of the next sub-step
+// into the registers that column Q just released.  The scheduling fences
+// keep this order: the compiler would otherwise hoist all LDS reads and hold
+// both fragment sets at once.
+template <int Q>
+__device__ __forceinline__ void slot(const GemmCtx& c, const uint8_t* rbuf, int rj, uint8_t* fb, uint8_t* sp,
+                                     __amdgpu_buffer_rsrc_t rd, uint32_t d_off, __amdgpu_buffer_rsrc_t rs,
+                                     uint32_t s_off, uint32_t lk, const Frags& cur, Frags& nxt, Stage& st,
+                                     v4f (&acc)[8][8]) {
+  mfma_iq<0, Q>(cur, acc[0][Q]);
+  nxt.b[Q] = *reinterpret_cast<const uint4*>(rbuf + kFragOp + (c.wn * 8 + Q) * 2048 + c.r_frag[rj]);
+  mfma_iq<1, Q>(cur, acc[1][Q]);
+  *reinterpret_cast<uint4*>(fb + (Q >> 1) * 2048 + ((Q & 1) ? c.w_frag1 : c.w_frag0)) = st.d[Q];
+  mfma_iq<2, Q>(cur, acc[2][Q]);
+  st.d[Q] = load16(rd, d_off + Q * c.row_step8, lk * 128);
+  mfma_iq<3, Q>(cur, acc[3][Q]);
+  sp[Q * 256] = static_cast<uint8_t>(((Q < 4) ? st.s.x : st.s.y) >> (8 * (Q % 4)));
+  mfma_iq<4, Q>(cur, acc[4][Q]);
+  if (Q == 7) st.s = load8(rs, s_off, lk * 8);
+  mfma_iq<5, Q>(cur, acc[5][Q]);
+  mfma_iq<6, Q>(cur, acc[6][Q]);
+  mfma_iq<7, Q>(cur, acc[7][Q]);
+  nxt.a[Q] = read_a(c, rbuf, rj, Q);
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// One phase: the MFMAs of the current sub-step on `cur`; meanwhile sub-step
+// (rbuf, rj) into `nxt`, operand `op` of the block staged in `st` written to
+// `wbuf`, and `st` reloaded with block `lk` of that operand.
+__device__ __forceinline__ void phase(const GemmCtx& c, const uint8_t* rbuf, int rj, uint8_t* wbuf, int op, int lk,
+                                      Frags& cur, Frags& nxt, Stage& st, v4f (&acc)[8][8]) {
+  __builtin_amdgcn_sched_barrier(0);
+  nxt.sa = *reinterpret_cast<const uint2*>(rbuf + 2 * kFragOp + rj * 1024 + c.r_scale_a);
+  nxt.sb = *reinterpret_cast<const uint2*>(rbuf + 2 * kFragOp + kScaleOp + rj * 1024 + c.r_scale_b);
+  uint8_t* const fb = wbuf + op * kFragOp + c.wave * (4 * 2048);
+  uint8_t* const sp = wbuf + 2 * kFragOp + op * kScaleOp + c.w_scale;
+  const __amdgpu_buffer_rsrc_t rd = op ? c.rb : c.ra, rs = op ? c.rsb : c.rsa;
+  const uint32_t d_off = op ? c.b_off : c.a_off, s_off = op ? c.sb_off : c.sa_off;
+  const uint32_t k = static_cast<uint32_t>(lk);
+  slot<0>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  slot<1>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  slot<2>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  slot<3>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  slot<4>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  slot<5>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  slot<6>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  slot<7>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  phase_barrier();
 }
 
 __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
                                                         const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
                                                         float* __restrict__ Y, int M, int N, int K) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
   GemmCtx c;
-  c.lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   c.wm = c.wave >> 1;
   c.wn = c.wave & 1;
-  c.nks = (K + 255) / 256;
-  c.half_tail = (K & 255) != 0;
+  const int nfull = K / 256;                 // >= 1 (checked by the launcher)
+  const bool half = (K & 255) != 0;          // a last block of one sub-step
+  c.nb = nfull + (half ? 1 : 0);
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
-  const int rr = c.lane & 15, grp = c.lane >> 4;
+  const int rr = lane & 15, grp = lane >> 4;
   // 32-bit byte offsets from uniform bases (the host checks every operand is
-  // below 2^31 bytes).  Rows past the edge read the last row (never stored).
-  // A K of 128 (mod 256) leaves a half step: its upper 64 bytes per row (and 4
-  // scale bytes) read past the row, the next row or zeros from the bounded
-  // descriptor, and feed only the sub-step that the last step skips.
+  // below 2^31 bytes).  Rows past the edge fall outside the buffer descriptor's
+  // bound and read as zeros (their outputs are never stored).  In a half block
+  // the upper 64 bytes of a row (and 4 of its 8 scale bytes) read the next
+  // row's data or zeros; they feed only the sub-step that is skipped.
   const uint32_t krow = static_cast<uint32_t>(K) / 2, srow = static_cast<uint32_t>(K) / 32;
-  const int lr = c.lane >> 3, lc = c.lane & 7;
-  const int ra = min(m0 + 64 * c.wave + lr, M - 1), rb = min(n0 + 64 * c.wave + lr, N - 1);
-  c.a_off = static_cast<uint32_t>(ra) * krow + lc * 16;
-  c.b_off = static_cast<uint32_t>(rb) * krow + lc * 16;
-  c.a_step8 = 8 * krow;
-  c.b_step8 = 8 * krow;
-  const int s_op = c.wave >> 1;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = (c.wave & 1) * 128 + 64 * u + c.lane;            // row within the tile
-    const int base = s_op ? n0 : m0, lim = s_op ? N - 1 : M - 1;
-    c.s_off[u] = static_cast<uint32_t>(min(base + row, lim)) * srow;
-    // scale position: lane row rr' = row % 16, then [sub-step][half = row / 128][i = (row / 16) % 8]
-    c.w_scale[u] = (row & 15) * kScalePitch + ((row >> 7) * 8 + ((row >> 4) & 7)) * 4;
-  }
-  // writer chunk position: row r = lr (+8 for odd u), logical chunk lc
-  c.w_frag = lr * 128 + ((lc ^ ((lr >> 1) & 7)) * 16);
+  const int lr = lane >> 3, lc = lane & 7;
+  c.a_off = static_cast<uint32_t>(m0 + 64 * c.wave + lr) * krow + lc * 16;
+  c.b_off = static_cast<uint32_t>(n0 + 64 * c.wave + lr) * krow + lc * 16;
+  c.row_step8 = 8 * krow;
+  c.w_frag0 = lr * 128 + ((lc ^ ((lr >> 1) & 7)) * 16);
   c.w_frag1 = (lr + 8) * 128 + ((lc ^ (((lr + 8) >> 1) & 7)) * 16);
-  // reader: row rr, logical chunk 4 j + grp
+  {
+    // scale loader: lane -> (rr, d) = (lane % 16, lane / 16) and this wave's
+    // tile position phase c4 = wave: tile row 128 (d / 2) + 16 (4 (d % 2) + c4) + rr,
+    // stored at byte [rr][4 d + c4] of each plane (dword rr * 4 + d: all distinct)
+    const int d = lane >> 4;
+    const int row = 128 * (d >> 1) + 16 * (4 * (d & 1) + c.wave) + rr;
+    c.sa_off = static_cast<uint32_t>(m0 + row) * srow;
+    c.sb_off = static_cast<uint32_t>(n0 + row) * srow;
+    c.w_scale = rr * 16 + 4 * d + c.wave;
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) c.r_frag[j] = rr * 128 + ((((4 * j + grp) ^ ((rr >> 1) & 7))) * 16);
-  c.r_scale_a = rr * kScalePitch + c.wm * 32;
-  c.r_scale_b = rr * kScalePitch + c.wn * 32;
-  // descriptors bound the operands exactly (out-of-range lanes read zeros)
+  c.r_scale_a = grp * 256 + rr * 16 + c.wm * 8;
+  c.r_scale_b = grp * 256 + rr * 16 + c.wn * 8;
   c.ra = make_rsrc(A, static_cast<uint32_t>(M) * krow);
   c.rb = make_rsrc(B, static_cast<uint32_t>(N) * krow);
-  c.rs = s_op ? make_rsrc(SB, static_cast<uint32_t>(N) * srow) : make_rsrc(SA, static_cast<uint32_t>(M) * srow);
+  c.rsa = make_rsrc(SA, static_cast<uint32_t>(M) * srow);
+  c.rsb = make_rsrc(SB, static_cast<uint32_t>(N) * srow);
 
   v4f acc[8][8];
 #pragma unroll
@@ -389,19 +425,53 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restri
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[i][q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  Staging g;
-  load_stage(c, 0, g);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  store_stage<0>(c, g);
-  load_stage(c, min(1, c.nks - 1), g);
+  uint8_t* const buf0 = smem;
+  uint8_t* const buf1 = smem + kStageBytes;
+  const int last = c.nb - 1;
+  // prologue: block 0 and block 1's A into LDS, block 1's B and block 2's A
+  // into the staging registers, sub-step (0, 0) into the first fragment set.
+  // Fenced so that the staging loads keep the order the main loop assumes
+  // (B before A).
+  Stage sa, sb;
+  Frags f0, f1;
+  load_op(c.ra, c.a_off, c.rsa, c.sa_off, c.row_step8, 0, sa);
+  load_op(c.rb, c.b_off, c.rsb, c.sb_off, c.row_step8, 0, sb);
+  __builtin_amdgcn_sched_barrier(0);
+  write_op(c, buf0, 0, sa);
+  write_op(c, buf0, 1, sb);
+  __builtin_amdgcn_sched_barrier(0);
+  load_op(c.ra, c.a_off, c.rsa, c.sa_off, c.row_step8, min(1, last), sa);
+  __builtin_amdgcn_sched_barrier(0);
+  load_op(c.rb, c.b_off, c.rsb, c.sb_off, c.row_step8, min(1, last), sb);
+  __builtin_amdgcn_sched_barrier(0);
+  write_op(c, buf1, 0, sa);
+  __builtin_amdgcn_sched_barrier(0);
+  load_op(c.ra, c.a_off, c.rsa, c.sa_off, c.row_step8, min(2, last), sa);
+  phase_barrier();
+  read_b_scales(c, buf0, 0, f0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) f0.a[q] = read_a(c, buf0, 0, q);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The loop runs at least once, so every path consumes the prologue's staging
+  // loads and the compiler cannot sink (and reorder) them past the loop entry.
   int k = 0;
 #pragma unroll 1
-  for (; k + 1 < c.nks; k += 2) {
-    k_step<0>(c, k, g, acc);
-    k_step<1>(c, k + 1, g, acc);
+  do {
+    uint8_t* const cb = (k & 1) ? buf1 : buf0;   // block k
+    uint8_t* const nb = (k & 1) ? buf0 : buf1;   // block k + 1
+    // sub-step (k, 0); read (k, 1); write B(k+1); load B(k+2)
+    phase(c, cb, 1, nb, 1, min(k + 2, last), f0, f1, sb, acc);
+    // sub-step (k, 1); read (k+1, 0); write A(k+2) into block k's buffer; load A(k+3)
+    phase(c, nb, 0, cb, 0, min(k + 3, last), f1, f0, sa, acc);
+    ++k;
+  } while (k < nfull);
+  if (half) {   // sub-step (nfull, 0), read by the last phase
+    mfma_column<0>(f0, acc); mfma_column<1>(f0, acc); mfma_column<2>(f0, acc); mfma_column<3>(f0, acc);
+    mfma_column<4>(f0, acc); mfma_column<5>(f0, acc); mfma_column<6>(f0, acc); mfma_column<7>(f0, acc);
   }
-  if (k < c.nks) k_step<0>(c, k, g, acc);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // surplus staging loads
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // surplus staging loads
 
   // lane holds Y[m0 + 128 wm + 16 q + rr][n0 + 128 wn + 16 i + 4 grp + 0..3]
 #pragma unroll
@@ -429,8 +499,11 @@ namespace wush {
 
 wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
                        float* Y, hipStream_t stream) {
-  const bool small = static_cast<long>(M) * (K / 2) < (1L << 31) && static_cast<long>(N) * (K / 2) < (1L << 31);
-  if (small) {
+  // LDS kernel: 32-bit offsets (operands below 2 GiB) and at least two
+  // 128-wide K half-steps
+  const bool lds = static_cast<long>(M) * (K / 2) < (1L << 31) && static_cast<long>(N) * (K / 2) < (1L << 31) &&
+                   K >= 256;
+  if (lds) {
     const long tiles = static_cast<long>((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     if (tiles > 0x7fffffffL) return fail(WUSH_E_SHAPE, "wush_w4a4_gemm: too many tiles");
     hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, SA, B, SB, Y, M,
