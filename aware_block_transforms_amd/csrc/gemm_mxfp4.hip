@@ -174,9 +174,11 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_direct(const uint8_t* __restri
 //   * j = 0: LDS writes of block k+1's B operand from its staging registers,
 //     then the global loads of block k+2's B into them;
 //     j = 1: the same for A, blocks k+2 and k+3,
-// then one workgroup barrier.  Two LDS block buffers (68 KB each); every
-// global load has two phases to land, and a buffer is rewritten only after the
-// barrier that follows its last read.
+// and after the j = 0 phase one workgroup barrier (one per block suffices: a
+// j = 1 phase reads block k+1 and writes block k's buffer, whose last reads
+// came before the barrier; the next barrier publishes both writes before any
+// wave reads them).  Two LDS block buffers (68 KB each); every global load has
+// two phases to land.
 //
 // Global -> registers: buffer_load_dwordx4 with lane (lr, lc) = (lane / 8,
 // lane % 8) fetching the 16-byte chunk lc of row lr: 8 full 128-byte rows
@@ -188,8 +190,11 @@ __global__ __launch_bounds__(256) void gemm_mxfp4_direct(const uint8_t* __restri
 // E8M0 scales, one byte each, as plane [sub-step j][K group g] of
 // [lane row rr][8 half + i] for tile row 128 half + 16 i + rr: a lane reads
 // the 8 scale bytes of its 8 fragments with one ds_read_b64 and the MFMA's
-// op_sel picks the byte.  The loaders write the planes byte by byte, with the
-// rows of one instruction chosen so that its 64 lanes hit 64 distinct dwords.
+// op_sel picks the byte; planes of odd K groups are rotated by 8 bytes so
+// that the lane groups of K groups 2m and 2m+1 read disjoint banks.  A small
+// pre-pass writes the scales in exactly this order, 2 KB per (row tile,
+// block), so that staging them is one contiguous 8-byte load and one
+// ds_write_b64 per lane (row-major scales would cost a cache line per row).
 //
 // Tile order: workgroups are dealt to the 8 XCDs round-robin (id % 8), so the
 // tile index is remapped to give each XCD a contiguous run of tiles, walked in
@@ -247,15 +252,17 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& t
 }
 
 struct Frags { uint4 a[8], b[8]; uint2 sa, sb; };   // sa / sb: 8 scale bytes, fragment i in byte i
-struct Stage { uint4 d[8]; uint2 s; };                // one operand of one block: this wave's 64 rows + 64 scale rows
+// one operand of one block: this wave's 64 rows of codes and its quarter
+// (512 bytes) of the block's scale planes
+struct Stage { uint4 d[8]; uint2 s; };
 
 struct GemmCtx {
   __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
   uint32_t a_off, b_off;         // loader: row 64 wave + lane / 8, chunk lane % 8 (+ u * row_step8 for instruction u)
   uint32_t row_step8;            // bytes of 8 rows
-  uint32_t sa_off, sb_off;       // loader: this lane's scale row (see kernel)
+  uint32_t sa_off, sb_off;       // this lane's 8 bytes of the tile's plane-ordered scales, block 0
   uint32_t w_frag0, w_frag1;     // LDS slot of the loader's chunk within a fragment pair (even / odd u)
-  uint32_t w_scale;              // LDS offset of the loader's scale byte within plane 0
+  uint32_t w_scale;              // LDS offset of the loader's 8 scale bytes within the operand's planes
   uint32_t r_frag[2];            // LDS slot of this lane's read chunk within a fragment pair, per sub-step
   uint32_t r_scale_a, r_scale_b; // LDS offset of this lane's 8 scale bytes within plane (0, g)
   int wave, wm, wn, nb;
@@ -264,8 +271,8 @@ struct GemmCtx {
 __device__ __forceinline__ void load_op(__amdgpu_buffer_rsrc_t rd, uint32_t d_off, __amdgpu_buffer_rsrc_t rs,
                                         uint32_t s_off, uint32_t step8, int k, Stage& g) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) g.d[u] = load16(rd, d_off + u * step8, static_cast<uint32_t>(k) * 128);
-  g.s = load8(rs, s_off, static_cast<uint32_t>(k) * 8);
+  for (int u = 0; u < 8; ++u) g.d[u] = load16(rd, d_off, static_cast<uint32_t>(k) * 128 + u * step8);
+  g.s = load8(rs, s_off, static_cast<uint32_t>(k) * kScaleOp);
 }
 
 // one operand (op 0 = A, 1 = B) of a block into the LDS buffer `buf`
@@ -274,12 +281,7 @@ __device__ __forceinline__ void write_op(const GemmCtx& c, uint8_t* buf, int op,
 #pragma unroll
   for (int u = 0; u < 8; ++u)
     *reinterpret_cast<uint4*>(fb + (u >> 1) * 2048 + ((u & 1) ? c.w_frag1 : c.w_frag0)) = g.d[u];
-  uint8_t* sp = buf + 2 * kFragOp + op * kScaleOp + c.w_scale;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    sp[b * 256] = static_cast<uint8_t>(g.s.x >> (8 * b));          // sub-step 0, K group b
-    sp[(4 + b) * 256] = static_cast<uint8_t>(g.s.y >> (8 * b));    // sub-step 1, K group b
-  }
+  *reinterpret_cast<uint2*>(buf + 2 * kFragOp + op * kScaleOp + c.w_scale) = g.s;
 }
 
 __device__ __forceinline__ uint4 read_a(const GemmCtx& c, const uint8_t* buf, int j, int q) {
@@ -319,27 +321,30 @@ __device__ __forceinline__ void mfma_column(const Frags& f, v4f (&acc)[8][8]) {
 
 // Slot Q of a phase: the 8 MFMAs of column Q of the current sub-step on
 // `cur`, interleaved with this slot's share of the memory work so that no
-// unit sees a burst: B fragment Q of the next sub-step into `nxt`, staging
+// unit sees a burst: B fragments 2Q and 2Q+1 of the next sub-step into `nxt`
+// (slots 0-3, so that they have landed when the next phase starts), staging
 // register Q written to LDS and reloaded from the next block of its operand,
 // scale plane Q written, and at the end A fragment Q of the next sub-step
 // into the registers that column Q just released.  The scheduling fences
 // keep this order: the compiler would otherwise hoist all LDS reads and hold
 // both fragment sets at once.
 template <int Q>
-__device__ __forceinline__ void slot(const GemmCtx& c, const uint8_t* rbuf, int rj, uint8_t* fb, uint8_t* sp,
+__device__ __forceinline__ void slot(const GemmCtx& c, const uint8_t* rbuf, int rj, uint8_t* fb, uint2* sp,
                                      __amdgpu_buffer_rsrc_t rd, uint32_t d_off, __amdgpu_buffer_rsrc_t rs,
                                      uint32_t s_off, uint32_t lk, const Frags& cur, Frags& nxt, Stage& st,
                                      v4f (&acc)[8][8]) {
   mfma_iq<0, Q>(cur, acc[0][Q]);
-  nxt.b[Q] = *reinterpret_cast<const uint4*>(rbuf + kFragOp + (c.wn * 8 + Q) * 2048 + c.r_frag[rj]);
+  if (Q < 4) nxt.b[2 * Q] = *reinterpret_cast<const uint4*>(rbuf + kFragOp + (c.wn * 8 + 2 * Q) * 2048 + c.r_frag[rj]);
   mfma_iq<1, Q>(cur, acc[1][Q]);
+  if (Q < 4)
+    nxt.b[2 * Q + 1] = *reinterpret_cast<const uint4*>(rbuf + kFragOp + (c.wn * 8 + 2 * Q + 1) * 2048 + c.r_frag[rj]);
   *reinterpret_cast<uint4*>(fb + (Q >> 1) * 2048 + ((Q & 1) ? c.w_frag1 : c.w_frag0)) = st.d[Q];
   mfma_iq<2, Q>(cur, acc[2][Q]);
-  st.d[Q] = load16(rd, d_off + Q * c.row_step8, lk * 128);
+  st.d[Q] = load16(rd, d_off, lk * 128 + Q * c.row_step8);
   mfma_iq<3, Q>(cur, acc[3][Q]);
-  sp[Q * 256] = static_cast<uint8_t>(((Q < 4) ? st.s.x : st.s.y) >> (8 * (Q % 4)));
+  if (Q == 6) *sp = st.s;
   mfma_iq<4, Q>(cur, acc[4][Q]);
-  if (Q == 7) st.s = load8(rs, s_off, lk * 8);
+  if (Q == 7) st.s = load8(rs, s_off, lk * kScaleOp);
   mfma_iq<5, Q>(cur, acc[5][Q]);
   mfma_iq<6, Q>(cur, acc[6][Q]);
   mfma_iq<7, Q>(cur, acc[7][Q]);
@@ -350,13 +355,14 @@ __device__ __forceinline__ void slot(const GemmCtx& c, const uint8_t* rbuf, int 
 // One phase: the MFMAs of the current sub-step on `cur`; meanwhile sub-step
 // (rbuf, rj) into `nxt`, operand `op` of the block staged in `st` written to
 // `wbuf`, and `st` reloaded with block `lk` of that operand.
+template <bool kBarrier>
 __device__ __forceinline__ void phase(const GemmCtx& c, const uint8_t* rbuf, int rj, uint8_t* wbuf, int op, int lk,
                                       Frags& cur, Frags& nxt, Stage& st, v4f (&acc)[8][8]) {
   __builtin_amdgcn_sched_barrier(0);
   nxt.sa = *reinterpret_cast<const uint2*>(rbuf + 2 * kFragOp + rj * 1024 + c.r_scale_a);
   nxt.sb = *reinterpret_cast<const uint2*>(rbuf + 2 * kFragOp + kScaleOp + rj * 1024 + c.r_scale_b);
   uint8_t* const fb = wbuf + op * kFragOp + c.wave * (4 * 2048);
-  uint8_t* const sp = wbuf + 2 * kFragOp + op * kScaleOp + c.w_scale;
+  uint2* const sp = reinterpret_cast<uint2*>(wbuf + 2 * kFragOp + op * kScaleOp + c.w_scale);
   const __amdgpu_buffer_rsrc_t rd = op ? c.rb : c.ra, rs = op ? c.rsb : c.rsa;
   const uint32_t d_off = op ? c.b_off : c.a_off, s_off = op ? c.sb_off : c.sa_off;
   const uint32_t k = static_cast<uint32_t>(lk);
@@ -368,11 +374,44 @@ __device__ __forceinline__ void phase(const GemmCtx& c, const uint8_t* rbuf, int
   slot<5>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
   slot<6>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
   slot<7>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
-  phase_barrier();
+  if (kBarrier) phase_barrier();
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA,
-                                                        const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB,
+// Scales in plane order: for each 256-row tile t and 256-wide K block k, the
+// 2 KB at (t nb + k) * 2048 hold the block's 8 planes exactly as the LDS
+// stage stores them (see above); rows past the operand and K groups past K
+// are zero.  One workgroup of 256 threads (thread = tile row) per row tile
+// and pair of blocks.  Tiles 0 .. tiles_a - 1 come from SA (ra rows), the
+// rest from SB (rb rows).
+__global__ __launch_bounds__(256) void scales_to_planes(const uint8_t* __restrict__ SA, int ra,
+                                                        const uint8_t* __restrict__ SB, int rb, int tiles_a, int K,
+                                                        int nb, uint8_t* __restrict__ P) {
+  __shared__ uint8_t planes[2 * kScaleOp];
+  const int t = blockIdx.x, k0 = 2 * blockIdx.y, tr = threadIdx.x;
+  const bool in_a = t < tiles_a;
+  const int row = (in_a ? t : t - tiles_a) * kBM + tr;
+  const int rows = in_a ? ra : rb;
+  const int sdw = K / 128;   // scale dwords per row
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(in_a ? SA : SB) + static_cast<size_t>(row) * sdw;
+  uint32_t v[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) v[d] = (row < rows && 2 * k0 + d < sdw) ? s32[2 * k0 + d] : 0u;
+  const int rr = tr & 15, pos = 8 * (tr >> 7) + ((tr >> 4) & 7);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      planes[kk * kScaleOp + b * 256 + rr * 16 + (pos ^ (8 * (b & 1)))] =
+          static_cast<uint8_t>(v[2 * kk + (b >> 2)] >> (8 * (b & 3)));
+  __syncthreads();
+  const int nk = min(2, nb - k0);   // 16 bytes per thread per block pair
+  if (tr * 16 < nk * kScaleOp)
+    *reinterpret_cast<uint4*>(P + (static_cast<size_t>(t) * nb + k0) * kScaleOp + tr * 16) =
+        reinterpret_cast<const uint4*>(planes)[tr];
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ PA,
+                                                        const uint8_t* __restrict__ B, const uint8_t* __restrict__ PB,
                                                         float* __restrict__ Y, int M, int N, int K) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
   GemmCtx c;
@@ -391,9 +430,9 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restri
   // 32-bit byte offsets from uniform bases (the host checks every operand is
   // below 2^31 bytes).  Rows past the edge fall outside the buffer descriptor's
   // bound and read as zeros (their outputs are never stored).  In a half block
-  // the upper 64 bytes of a row (and 4 of its 8 scale bytes) read the next
-  // row's data or zeros; they feed only the sub-step that is skipped.
-  const uint32_t krow = static_cast<uint32_t>(K) / 2, srow = static_cast<uint32_t>(K) / 32;
+  // the upper 64 bytes of a row read the next row's data or zeros; they feed
+  // only the sub-step that is skipped.
+  const uint32_t krow = static_cast<uint32_t>(K) / 2;
   const int lr = lane >> 3, lc = lane & 7;
   c.a_off = static_cast<uint32_t>(m0 + 64 * c.wave + lr) * krow + lc * 16;
   c.b_off = static_cast<uint32_t>(n0 + 64 * c.wave + lr) * krow + lc * 16;
@@ -401,23 +440,22 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restri
   c.w_frag0 = lr * 128 + ((lc ^ ((lr >> 1) & 7)) * 16);
   c.w_frag1 = (lr + 8) * 128 + ((lc ^ (((lr + 8) >> 1) & 7)) * 16);
   {
-    // scale loader: lane -> (rr, d) = (lane % 16, lane / 16) and this wave's
-    // tile position phase c4 = wave: tile row 128 (d / 2) + 16 (4 (d % 2) + c4) + rr,
-    // stored at byte [rr][4 d + c4] of each plane (dword rr * 4 + d: all distinct)
-    const int d = lane >> 4;
-    const int row = 128 * (d >> 1) + 16 * (4 * (d & 1) + c.wave) + rr;
-    c.sa_off = static_cast<uint32_t>(m0 + row) * srow;
-    c.sb_off = static_cast<uint32_t>(n0 + row) * srow;
-    c.w_scale = rr * 16 + 4 * d + c.wave;
+    // scales arrive already in plane order, one 2 KB block per (row tile,
+    // K block): wave w copies bytes 512 w + 8 lane .. + 7
+    c.w_scale = c.wave * 512 + lane * 8;
+    c.sa_off = static_cast<uint32_t>(tm * c.nb) * kScaleOp + c.w_scale;
+    c.sb_off = static_cast<uint32_t>(tn * c.nb) * kScaleOp + c.w_scale;
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) c.r_frag[j] = rr * 128 + ((((4 * j + grp) ^ ((rr >> 1) & 7))) * 16);
-  c.r_scale_a = grp * 256 + rr * 16 + c.wm * 8;
-  c.r_scale_b = grp * 256 + rr * 16 + c.wn * 8;
+  // odd K groups keep their planes rotated by 8 bytes, so that the two lane
+  // groups of a ds_read_b64 half (K groups 2m and 2m+1) use disjoint banks
+  c.r_scale_a = grp * 256 + rr * 16 + ((c.wm * 8) ^ (8 * (grp & 1)));
+  c.r_scale_b = grp * 256 + rr * 16 + ((c.wn * 8) ^ (8 * (grp & 1)));
   c.ra = make_rsrc(A, static_cast<uint32_t>(M) * krow);
   c.rb = make_rsrc(B, static_cast<uint32_t>(N) * krow);
-  c.rsa = make_rsrc(SA, static_cast<uint32_t>(M) * srow);
-  c.rsb = make_rsrc(SB, static_cast<uint32_t>(N) * srow);
+  c.rsa = make_rsrc(PA, static_cast<uint32_t>(tiles_m * c.nb) * kScaleOp);
+  c.rsb = make_rsrc(PB, static_cast<uint32_t>(tiles_n * c.nb) * kScaleOp);
 
   v4f acc[8][8];
 #pragma unroll
@@ -461,10 +499,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restri
   do {
     uint8_t* const cb = (k & 1) ? buf1 : buf0;   // block k
     uint8_t* const nb = (k & 1) ? buf0 : buf1;   // block k + 1
-    // sub-step (k, 0); read (k, 1); write B(k+1); load B(k+2)
-    phase(c, cb, 1, nb, 1, min(k + 2, last), f0, f1, sb, acc);
-    // sub-step (k, 1); read (k+1, 0); write A(k+2) into block k's buffer; load A(k+3)
-    phase(c, nb, 0, cb, 0, min(k + 3, last), f1, f0, sa, acc);
+    // sub-step (k, 0); read (k, 1); write B(k+1); load B(k+2); barrier
+    phase<true>(c, cb, 1, nb, 1, min(k + 2, last), f0, f1, sb, acc);
+    // sub-step (k, 1); read (k+1, 0); write A(k+2) into block k's buffer; load A(k+3).
+    // No barrier: block k's buffer was last read before the barrier above,
+    // and A(k+2) is next read after the barrier that ends the next phase.
+    phase<false>(c, nb, 0, cb, 0, min(k + 3, last), f1, f0, sa, acc);
     ++k;
   } while (k < nfull);
   if (half) {   // sub-step (nfull, 0), read by the last phase
@@ -504,15 +544,29 @@ wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA,
   const bool lds = static_cast<long>(M) * (K / 2) < (1L << 31) && static_cast<long>(N) * (K / 2) < (1L << 31) &&
                    K >= 256;
   if (lds) {
-    const long tiles = static_cast<long>((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    if (tiles > 0x7fffffffL) return fail(WUSH_E_SHAPE, "wush_w4a4_gemm: too many tiles");
-    hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, SA, B, SB, Y, M,
-                       N, K);
-  } else {
-    dim3 grid((N + kBlockN - 1) / kBlockN, (M + kBlockM - 1) / kBlockM);
-    if (grid.y > 65535u) return fail(WUSH_E_SHAPE, "wush_w4a4_gemm: M=%d too large", M);
-    hipLaunchKernelGGL(gemm_mxfp4_direct, grid, dim3(256), 0, stream, A, SA, B, SB, Y, M, N, K);
+    const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN, nb = (K + 255) / 256;
+    const long tiles = static_cast<long>(tiles_m) * tiles_n;
+    if (tiles > 0x7fffffffL || tiles_m > 65535 || tiles_n > 65535)
+      return fail(WUSH_E_SHAPE, "wush_w4a4_gemm: too many tiles");
+    // plane-ordered scales in stream-ordered scratch, freed after the kernel
+    const size_t pa_bytes = static_cast<size_t>(tiles_m) * nb * kScaleOp;
+    const size_t p_bytes = pa_bytes + static_cast<size_t>(tiles_n) * nb * kScaleOp;
+    uint8_t* P = nullptr;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&P), p_bytes, stream);
+    if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm scratch (%zu bytes): %s", p_bytes, hipGetErrorString(e));
+    hipLaunchKernelGGL(scales_to_planes, dim3(tiles_m + tiles_n, (nb + 1) / 2), dim3(256), 0, stream, SA, M, SB, N,
+                       tiles_m, K, nb, P);
+    hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, P, B,
+                       P + pa_bytes, Y, M, N, K);
+    e = hipGetLastError();
+    const hipError_t f = hipFreeAsync(P, stream);
+    if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm launch: %s", hipGetErrorString(e));
+    if (f != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm scratch free: %s", hipGetErrorString(f));
+    return WUSH_OK;
   }
+  dim3 grid((N + kBlockN - 1) / kBlockN, (M + kBlockM - 1) / kBlockM);
+  if (grid.y > 65535u) return fail(WUSH_E_SHAPE, "wush_w4a4_gemm: M=%d too large", M);
+  hipLaunchKernelGGL(gemm_mxfp4_direct, grid, dim3(256), 0, stream, A, SA, B, SB, Y, M, N, K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm launch: %s", hipGetErrorString(e));
   return WUSH_OK;
