@@ -8,10 +8,12 @@
 // "The gist": transform and quantizer run as one fused GPU kernel.
 //
 // Work mapping (CDNA4, wave64):
-//  * one wave owns one block b of channels and walks token tiles of 64; lane
-//    l holds token (tile*64 + l).  The block's bs x bs matrix is identical for
-//    every lane, so it is read with scalar loads into SGPRs and broadcast to
-//    the FMAs for free; the wave's x values stay in VGPRs.
+//  * one wave owns one block b of channels and two tiles of 64 tokens; lane
+//    l holds tokens base + l and base + 64 + l.  The block's bs x bs matrix is
+//    identical for every lane, so it is read with scalar loads into SGPRs and
+//    broadcast to the FMAs for free, each element serving both tokens (the
+//    scalar cache's bandwidth, not the VALU, bounds a one-token loop); the
+//    wave's x values stay in VGPRs.
 //  * y_i = fma chain over k (ascending, from +0) in fp32: bs*bs v_fma_f32 per
 //    lane and block.  All bs outputs of a block live in one lane, so the block
 //    maximum needs no cross-lane reduction.
@@ -30,7 +32,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;
-constexpr int kTileIters = 2;   // 64-token tiles per wave
+constexpr int kTokensPerWave = 2 * kWave;   // two 64-token tiles per wave
 
 enum Fmt { kMX = 0, kNV = 1, kI4 = 2, kAmax = 3 };
 
@@ -90,15 +92,37 @@ __device__ __forceinline__ void load_block(const void* __restrict__ X, size_t of
   }
 }
 
-// y = T x with the pinned fp32 FMA chain.  Tb is wave-uniform.
+// y = T x for two tokens at once, each with the pinned fp32 FMA chain.  Tb is
+// wave-uniform (scalar loads into SGPRs); every T element fetched through the
+// scalar cache feeds two FMAs, which halves the scalar-cache traffic that
+// otherwise bounds this kernel.
+// Rows of T are double-buffered in SGPRs: row i+1 is requested before the
+// FMAs of row i, and the fences keep the compiler from hoisting every row's
+// loads (which runs out of SGPRs and spills them to VGPR lanes).
 template <int BS>
-__device__ __forceinline__ void transform(const float* __restrict__ Tb, const float (&x)[BS], float (&y)[BS]) {
+__device__ __forceinline__ void transform2(const float* __restrict__ Tb, const float (&x0)[BS], const float (&x1)[BS],
+                                           float (&y0)[BS], float (&y1)[BS]) {
+  float tc[BS], tn[BS];
+#pragma unroll
+  for (int k = 0; k < BS; ++k) tc[k] = Tb[k];
 #pragma unroll
   for (int i = 0; i < BS; ++i) {
-    float acc = 0.0f;
+    if (i + 1 < BS) {
 #pragma unroll
-    for (int k = 0; k < BS; ++k) acc = __builtin_fmaf(Tb[i * BS + k], x[k], acc);
-    y[i] = acc;
+      for (int k = 0; k < BS; ++k) tn[k] = Tb[(i + 1) * BS + k];
+    }
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < BS; ++k) {
+      a0 = __builtin_fmaf(tc[k], x0[k], a0);
+      a1 = __builtin_fmaf(tc[k], x1[k], a1);
+    }
+    y0[i] = a0;
+    y1[i] = a1;
+#pragma unroll
+    for (int k = 0; k < BS; ++k) tc[k] = tn[k];
+    asm volatile("" ::: "memory");   // keeps the next row's loads here at the IR level too
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -130,9 +154,74 @@ __device__ __forceinline__ void store_codes(uint8_t* __restrict__ dst, const uin
   }
 }
 
+// Codes and scale of one token's block y (the pinned encoders); `amax` pass
+// only folds the block maximum into run_max.
+template <int BS, int FMT>
+__device__ __forceinline__ void encode_store(const float (&y)[BS], size_t row, int blk, int nblk, int d_in, float g,
+                                             uint8_t* __restrict__ codes, void* __restrict__ scales,
+                                             uint32_t& run_max) {
+  uint32_t ab = 0;
+#pragma unroll
+  for (int k = 0; k < BS; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
+  const bool bad = ab >= 0x7f800000u;          // NaN or Inf in the block
+  if constexpr (FMT == kAmax) {
+    run_max = max(run_max, ab);
+    return;
+  } else {
+    uint32_t w[BS / 8];
+#pragma unroll
+    for (int q = 0; q < BS / 8; ++q) w[q] = 0u;
+    if constexpr (FMT == kMX) {
+      const uint32_t ex = ab >> 23;
+      const uint32_t sbyte = ex > 2u ? ex - 2u : 0u;             // e + 127
+      const float inv = __uint_as_float((254u - sbyte) << 23);   // 2^-e
+#pragma unroll
+      for (int k = 0; k < BS / 2; ++k) w[k >> 2] = cvt_pair(w[k >> 2], y[2 * k] * inv, y[2 * k + 1] * inv, k & 3);
+      if (bad) zero_words(w);
+      reinterpret_cast<uint8_t*>(scales)[row * nblk + blk] = bad ? 0xffu : static_cast<uint8_t>(sbyte);
+    } else if constexpr (FMT == kNV) {
+      const float a = __uint_as_float(ab);
+      float s = fminf(a / (6.0f * g), 448.0f);
+      const uint32_t s8 = bad ? 0u : e4m3_encode(s);
+      const float s_eff = e4m3_decode(s8) * g;
+      const float r = 1.0f / s_eff;
+      const bool zero = bad || s_eff == 0.0f;
+      if (r <= 3.0e38f) {                       // finite r: every y * r is a number
+#pragma unroll
+        for (int k = 0; k < BS / 2; ++k) w[k >> 2] = cvt_pair(w[k >> 2], y[2 * k] * r, y[2 * k + 1] * r, k & 3);
+      } else {                                  // s_eff below 2^-128: 0 * inf is NaN -> code 0
+#pragma unroll
+        for (int k = 0; k < BS; ++k) w[k >> 3] |= e2m1_code_nan0(y[k] * r) << (4 * (k & 7));
+      }
+      if (zero) zero_words(w);
+      reinterpret_cast<uint8_t*>(scales)[row * nblk + blk] = bad ? 0x7fu : static_cast<uint8_t>(s8);
+    } else {  // INT4
+      const float a = __uint_as_float(ab);
+      const _Float16 h = static_cast<_Float16>(a / 7.0f);        // RNE
+      const float s32 = static_cast<float>(h);
+      const float r = 1.0f / s32;
+      const bool zero = bad || s32 == 0.0f;
+      // clamp to [-7, 7], then add 1.5 * 2^23: the fp32 add rounds to the nearest
+      // integer (ties to even) and leaves q in the low mantissa bits (two's complement)
+#pragma unroll
+      for (int k = 0; k < BS; ++k) {
+        const float t = __builtin_amdgcn_fmed3f(y[k] * r, -7.0f, 7.0f) + 12582912.0f;
+        w[k >> 3] |= (__float_as_uint(t) & 15u) << (4 * (k & 7));
+      }
+      if (zero) zero_words(w);
+      uint16_t hb;
+      __builtin_memcpy(&hb, &h, 2);
+      reinterpret_cast<uint16_t*>(scales)[row * nblk + blk] = bad ? static_cast<uint16_t>(0x7e00u) : hb;
+    }
+    store_codes<BS>(codes + row * (d_in / 2) + static_cast<size_t>(blk) * (BS / 2), w);
+  }
+}
+
 // One kernel for the three formats plus an amax-only pass (NVFP4 tensor scale).
+// A wave owns one block and two 64-token tiles: lane l transforms tokens
+// base + l and base + 64 + l together (see transform2).
 template <int BS, int FMT, bool BF16, bool IDENT>
-__global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_kernel(
+__global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves_per_eu(4))) void tq_kernel(
     const void* __restrict__ X, const float* __restrict__ T, int n, int d_in, float g,
     uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -141,92 +230,33 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_kernel(
   const int blk = blockIdx.x * kWavesPerGroup + wave;
   if (blk >= nblk) return;                       // wave-uniform
   const float* __restrict__ Tb = IDENT ? nullptr : T + static_cast<size_t>(blk) * BS * BS;
-  const int tok_base = blockIdx.y * (kWave * kTileIters);
+  const int tok0 = blockIdx.y * (2 * kWave) + lane, tok1 = tok0 + kWave;
+  const bool v0 = tok0 < n, v1 = tok1 < n;
   uint32_t run_max = 0;
 
-  // NVFP4 constants (uniform)
-  const float d6 = 6.0f * g;
-
-  float xn[BS];
-  int tok = tok_base + lane;
-  if (tok < n) load_block<BS, BF16>(X, static_cast<size_t>(tok) * d_in + static_cast<size_t>(blk) * BS, xn);
-
-#pragma unroll 1
-  for (int it = 0; it < kTileIters; ++it) {
-    float x[BS];
+  float x0[BS], x1[BS];
+  const size_t col = static_cast<size_t>(blk) * BS;
+  if (v0) load_block<BS, BF16>(X, static_cast<size_t>(tok0) * d_in + col, x0);
+  if (v1) load_block<BS, BF16>(X, static_cast<size_t>(tok1) * d_in + col, x1);
+  else {
 #pragma unroll
-    for (int k = 0; k < BS; ++k) x[k] = xn[k];
-    const bool valid = tok < n;
-    const int tok_next = tok + kWave;
-    if (it + 1 < kTileIters && tok_next < n)
-      load_block<BS, BF16>(X, static_cast<size_t>(tok_next) * d_in + static_cast<size_t>(blk) * BS, xn);
-
-    float y[BS];
-    if constexpr (IDENT) {
-#pragma unroll
-      for (int k = 0; k < BS; ++k) y[k] = x[k];
-    } else {
-      transform<BS>(Tb, x, y);
-    }
-    uint32_t ab = 0;
-#pragma unroll
-    for (int k = 0; k < BS; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
-    const bool bad = ab >= 0x7f800000u;          // NaN or Inf in the block
-
-    if constexpr (FMT == kAmax) {
-      if (valid) run_max = max(run_max, ab);
-    } else if (valid) {
-      const size_t row = static_cast<size_t>(tok);
-      uint32_t w[BS / 8];
-#pragma unroll
-      for (int q = 0; q < BS / 8; ++q) w[q] = 0u;
-      if constexpr (FMT == kMX) {
-        const uint32_t ex = ab >> 23;
-        const uint32_t sbyte = ex > 2u ? ex - 2u : 0u;             // e + 127
-        const float inv = __uint_as_float((254u - sbyte) << 23);   // 2^-e
-#pragma unroll
-        for (int k = 0; k < BS / 2; ++k) w[k >> 2] = cvt_pair(w[k >> 2], y[2 * k] * inv, y[2 * k + 1] * inv, k & 3);
-        if (bad) zero_words(w);
-        reinterpret_cast<uint8_t*>(scales)[row * nblk + blk] = bad ? 0xffu : static_cast<uint8_t>(sbyte);
-      } else if constexpr (FMT == kNV) {
-        const float a = __uint_as_float(ab);
-        float s = fminf(a / d6, 448.0f);
-        const uint32_t s8 = bad ? 0u : e4m3_encode(s);
-        const float s_eff = e4m3_decode(s8) * g;
-        const float r = 1.0f / s_eff;
-        const bool zero = bad || s_eff == 0.0f;
-        if (r <= 3.0e38f) {                       // finite r: every y * r is a number
-#pragma unroll
-          for (int k = 0; k < BS / 2; ++k) w[k >> 2] = cvt_pair(w[k >> 2], y[2 * k] * r, y[2 * k + 1] * r, k & 3);
-        } else {                                  // s_eff below 2^-128: 0 * inf is NaN -> code 0
-#pragma unroll
-          for (int k = 0; k < BS; ++k) w[k >> 3] |= e2m1_code_nan0(y[k] * r) << (4 * (k & 7));
-        }
-        if (zero) zero_words(w);
-        reinterpret_cast<uint8_t*>(scales)[row * nblk + blk] = bad ? 0x7fu : static_cast<uint8_t>(s8);
-      } else {  // INT4
-        const float a = __uint_as_float(ab);
-        const _Float16 h = static_cast<_Float16>(a / 7.0f);        // RNE
-        const float s32 = static_cast<float>(h);
-        const float r = 1.0f / s32;
-        const bool zero = bad || s32 == 0.0f;
-        // clamp to [-7, 7], then add 1.5 * 2^23: the fp32 add rounds to the nearest
-        // integer (ties to even) and leaves q in the low mantissa bits (two's complement)
-#pragma unroll
-        for (int k = 0; k < BS; ++k) {
-          const float t = __builtin_amdgcn_fmed3f(y[k] * r, -7.0f, 7.0f) + 12582912.0f;
-          w[k >> 3] |= (__float_as_uint(t) & 15u) << (4 * (k & 7));
-        }
-        if (zero) zero_words(w);
-        uint16_t hb;
-        __builtin_memcpy(&hb, &h, 2);
-        reinterpret_cast<uint16_t*>(scales)[row * nblk + blk] = bad ? static_cast<uint16_t>(0x7e00u) : hb;
-      }
-      store_codes<BS>(codes + row * (d_in / 2) + static_cast<size_t>(blk) * (BS / 2), w);
-    }
-    tok = tok_next;
-    if (tok_base + (it + 1) * kWave >= n) break;  // wave-uniform early exit
+    for (int k = 0; k < BS; ++k) x1[k] = 0.0f;
   }
+
+  float y0[BS], y1[BS];
+  if constexpr (IDENT) {
+#pragma unroll
+    for (int k = 0; k < BS; ++k) { y0[k] = x0[k]; y1[k] = x1[k]; }
+  } else {
+    transform2<BS>(Tb, x0, x1, y0, y1);
+    // materialize both tokens' outputs here: left alone, the compiler sinks
+    // each token's FMAs into its (divergent) store branch, and the T values
+    // both branches share then pile up in SGPRs
+#pragma unroll
+    for (int k = 0; k < BS; ++k) asm volatile("" : "+v"(y0[k]), "+v"(y1[k]));
+  }
+  if (v0) encode_store<BS, FMT>(y0, static_cast<size_t>(tok0), blk, nblk, d_in, g, codes, scales, run_max);
+  if (v1) encode_store<BS, FMT>(y1, static_cast<size_t>(tok1), blk, nblk, d_in, g, codes, scales, run_max);
 
   if constexpr (FMT == kAmax) {
 #pragma unroll
@@ -267,7 +297,7 @@ wush_status launch(int fmt, int bs, bool bf16, int n, int d_in, const void* X, c
   KernelFn k = select_kernel(fmt, bs, bf16, T == nullptr);
   if (!k) return wush::fail(WUSH_E_UNSUPPORTED, "transform_quant: no kernel for fmt=%d bs=%d", fmt, bs);
   const int nblk = d_in / bs;
-  dim3 grid((nblk + kWavesPerGroup - 1) / kWavesPerGroup, (n + kWave * kTileIters - 1) / (kWave * kTileIters));
+  dim3 grid((nblk + kWavesPerGroup - 1) / kWavesPerGroup, (n + kTokensPerWave - 1) / kTokensPerWave);
   if (grid.y > 65535u) return wush::fail(WUSH_E_SHAPE, "transform_quant: n=%d too large", n);
   hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, T, n, d_in, g, codes, scales, amax);
   hipError_t e = hipGetLastError();
