@@ -158,7 +158,13 @@ wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float*
  *   Y: device out, [M][N] fp32.
  * MXFP4 runs on the gfx950 block-scaled FP4 matrix cores; NVFP4 and INT4 use
  * exact dequantization to bf16 / int8 matrix cores with per-block scaling.
- * Errors: WUSH_E_ARG, WUSH_E_SHAPE (M, N < 1; K < 1 or K % 128), WUSH_E_HIP. */
+ * Asynchronous on `stream`.  For MXFP4 with K >= 256 the call takes
+ * (ceil(M/256) + ceil(N/256)) * ceil(K/256) * 2048 bytes of stream-ordered
+ * scratch (hipMallocAsync / hipFreeAsync on `stream`, from the device's
+ * default memory pool) for the scales re-laid in the kernel's order; the
+ * caller's buffers are only read (A, B) or written (Y).
+ * Errors: WUSH_E_ARG, WUSH_E_SHAPE (M, N < 1; K < 1 or K % 128), WUSH_E_HIP
+ * (launch failure, or the scratch could not be allocated). */
 wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K,
                            const uint8_t* a_codes, const void* a_scales, float a_g,
                            const uint8_t* b_codes, const void* b_scales, float b_g,
