@@ -44,11 +44,13 @@ _SIGS = {
     "wush_transform_quant": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _p], _i),
     "wush_nvfp4_global_scale": ([_i, _i, _i, _p, _p, _fp, _p], _i),
     "wush_pack_weights": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
-    "wush_w4a4_gemm": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _f, _p, _p], _i),
+    "wush_w4a4_gemm_ws_bytes": ([_i, _i, _i, _i], _sz),
+    "wush_w4a4_gemm": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _f, _p, _p, _sz, _p], _i),
     "wush_layer_loss": ([_i, _i, _p, _p, _p, _p, _p], _i),
     "wush_loss_ws_bytes": ([_i, _i], _sz),
     "wush_had256_pack_weights": ([_i, _i, _p, _p, _p, _p], _i),
-    "wush_had256_gemv": ([_i, _i, _i, _p, _p, _p, _p, _p], _i),
+    "wush_had256_gemv_ws_bytes": ([_i, _i], _sz),
+    "wush_had256_gemv": ([_i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
     "wush_had256_rotate": ([_i, _i, _p, _p, _p], _i),
     "wush_status_string": ([_i], ctypes.c_char_p),
     "wush_last_error": ([], ctypes.c_char_p),
@@ -144,11 +146,23 @@ def wush_pack_weights(fmt, W, Tw, codes, scales, stream=None):
     return g.value
 
 
-def wush_w4a4_gemm(fmt, a_codes, a_scales, b_codes, b_scales, Y, a_g=1.0, b_g=1.0, stream=None):
+def _ws(ws):
+    """(pointer, bytes) of an optional device workspace tensor."""
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def wush_w4a4_gemm_ws_bytes(fmt, M, N, K):
+    return lib.wush_w4a4_gemm_ws_bytes(_fmt(fmt), M, N, K)
+
+
+def wush_w4a4_gemm(fmt, a_codes, a_scales, b_codes, b_scales, Y, a_g=1.0, b_g=1.0, ws=None, stream=None):
     M, N = Y.shape
     K = a_codes.shape[1] * 2
+    wp, wb = _ws(ws)
     _check(lib.wush_w4a4_gemm(_fmt(fmt), M, N, K, _ptr(a_codes), _ptr(a_scales), float(a_g), _ptr(b_codes),
-                              _ptr(b_scales), float(b_g), _ptr(Y), _stream(stream)), "wush_w4a4_gemm")
+                              _ptr(b_scales), float(b_g), _ptr(Y), wp, wb, _stream(stream)), "wush_w4a4_gemm")
 
 
 def wush_loss_ws_bytes(M, N):
@@ -167,10 +181,15 @@ def wush_had256_pack_weights(W, planes, scales, stream=None):
            "wush_had256_pack_weights")
 
 
-def wush_had256_gemv(x, planes, scales, y, stream=None):
+def wush_had256_gemv_ws_bytes(batch, d_in):
+    return lib.wush_had256_gemv_ws_bytes(batch, d_in)
+
+
+def wush_had256_gemv(x, planes, scales, y, ws=None, stream=None):
     batch, d_in = x.shape
     d_out = y.shape[1]
-    _check(lib.wush_had256_gemv(batch, d_out, d_in, _ptr(x), _ptr(planes), _ptr(scales), _ptr(y),
+    wp, wb = _ws(ws)
+    _check(lib.wush_had256_gemv(batch, d_out, d_in, _ptr(x), _ptr(planes), _ptr(scales), _ptr(y), wp, wb,
                                 _stream(stream)), "wush_had256_gemv")
 
 

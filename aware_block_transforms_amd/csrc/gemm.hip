@@ -12,17 +12,22 @@
 #include "common.h"
 
 namespace wush {
+size_t gemm_mxfp4_ws_bytes(int M, int N, int K);
 wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
-                       float* Y, hipStream_t stream);
+                       float* Y, void* ws, size_t ws_bytes, hipStream_t stream);
 wush_status gemm_nvfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, float ga, const uint8_t* B,
                        const uint8_t* SB, float gb, float* Y, hipStream_t stream);
 wush_status gemm_int4(int M, int N, int K, const uint8_t* A, const uint16_t* SA, const uint8_t* B,
                       const uint16_t* SB, float* Y, hipStream_t stream);
 }  // namespace wush
 
+extern "C" size_t wush_w4a4_gemm_ws_bytes(wush_format fmt, int M, int N, int K) {
+  return fmt == WUSH_MXFP4 ? wush::gemm_mxfp4_ws_bytes(M, N, K) : 0;
+}
+
 extern "C" wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K, const uint8_t* a_codes,
                                       const void* a_scales, float a_g, const uint8_t* b_codes, const void* b_scales,
-                                      float b_g, float* Y, void* stream) {
+                                      float b_g, float* Y, void* ws, size_t ws_bytes, void* stream) {
   if (wush_format_block(fmt) == 0) return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: bad format %d", static_cast<int>(fmt));
   if (M < 1 || N < 1 || K < 128 || K % 128)
     return wush::fail(WUSH_E_SHAPE, "wush_w4a4_gemm: need M, N >= 1 and K a positive multiple of 128 (M=%d N=%d K=%d)",
@@ -31,11 +36,12 @@ extern "C" wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K, cons
   if (!wush::aligned16(a_codes) || !wush::aligned16(b_codes) || !wush::aligned16(Y) ||
       (reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(b_scales) & 3u))
     return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: codes and Y must be 16-byte aligned, scales 4-byte aligned");
+  if (ws && !wush::aligned16(ws)) return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (fmt) {
     case WUSH_MXFP4:
       return wush::gemm_mxfp4(M, N, K, a_codes, static_cast<const uint8_t*>(a_scales), b_codes,
-                              static_cast<const uint8_t*>(b_scales), Y, s);
+                              static_cast<const uint8_t*>(b_scales), Y, ws, ws_bytes, s);
     case WUSH_NVFP4:
       if (!(a_g > 0.0f && a_g < 3.0e38f) || !(b_g > 0.0f && b_g < 3.0e38f))
         return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: NVFP4 tensor scales must be positive and finite");

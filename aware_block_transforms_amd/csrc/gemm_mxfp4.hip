@@ -537,29 +537,45 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restri
 
 namespace wush {
 
+namespace {
+// LDS kernel: 32-bit offsets (operands below 2 GiB) and at least two 128-wide
+// K half-steps
+bool use_lds_kernel(int M, int N, int K) {
+  return static_cast<long>(M) * (K / 2) < (1L << 31) && static_cast<long>(N) * (K / 2) < (1L << 31) && K >= 256;
+}
+}  // namespace
+
+// bytes of plane-ordered scales the LDS kernel needs (0 for the direct kernel)
+size_t gemm_mxfp4_ws_bytes(int M, int N, int K) {
+  if (M < 1 || N < 1 || K < 1 || !use_lds_kernel(M, N, K)) return 0;
+  const size_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN, nb = (K + 255) / 256;
+  return (tiles_m + tiles_n) * nb * kScaleOp;
+}
+
 wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
-                       float* Y, hipStream_t stream) {
-  // LDS kernel: 32-bit offsets (operands below 2 GiB) and at least two
-  // 128-wide K half-steps
-  const bool lds = static_cast<long>(M) * (K / 2) < (1L << 31) && static_cast<long>(N) * (K / 2) < (1L << 31) &&
-                   K >= 256;
-  if (lds) {
+                       float* Y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (use_lds_kernel(M, N, K)) {
     const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN, nb = (K + 255) / 256;
     const long tiles = static_cast<long>(tiles_m) * tiles_n;
     if (tiles > 0x7fffffffL || tiles_m > 65535 || tiles_n > 65535)
       return fail(WUSH_E_SHAPE, "wush_w4a4_gemm: too many tiles");
-    // plane-ordered scales in stream-ordered scratch, freed after the kernel
+    // plane-ordered scales: the caller's workspace, else stream-ordered scratch
     const size_t pa_bytes = static_cast<size_t>(tiles_m) * nb * kScaleOp;
-    const size_t p_bytes = pa_bytes + static_cast<size_t>(tiles_n) * nb * kScaleOp;
-    uint8_t* P = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&P), p_bytes, stream);
-    if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm scratch (%zu bytes): %s", p_bytes, hipGetErrorString(e));
+    const size_t p_bytes = gemm_mxfp4_ws_bytes(M, N, K);
+    uint8_t* P = static_cast<uint8_t*>(ws);
+    if (P) {
+      if (ws_bytes < p_bytes) return fail(WUSH_E_ARG, "wush_w4a4_gemm: workspace of %zu bytes, need %zu", ws_bytes, p_bytes);
+    } else {
+      const hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&P), p_bytes, stream);
+      if (e != hipSuccess)
+        return fail(WUSH_E_HIP, "wush_w4a4_gemm scratch (%zu bytes): %s", p_bytes, hipGetErrorString(e));
+    }
     hipLaunchKernelGGL(scales_to_planes, dim3(tiles_m + tiles_n, (nb + 1) / 2), dim3(256), 0, stream, SA, M, SB, N,
                        tiles_m, K, nb, P);
     hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, P, B,
                        P + pa_bytes, Y, M, N, K);
-    e = hipGetLastError();
-    const hipError_t f = hipFreeAsync(P, stream);
+    const hipError_t e = hipGetLastError();
+    const hipError_t f = ws ? hipSuccess : hipFreeAsync(P, stream);
     if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm launch: %s", hipGetErrorString(e));
     if (f != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm scratch free: %s", hipGetErrorString(f));
     return WUSH_OK;

@@ -52,6 +52,7 @@ class W4A4Layer:
         self.w_g = W.wush_pack_weights(fmt, Wd, self.Tw, self.w_codes, self.w_scales)
         del Wd
         self.x_g = 1.0
+        self._ws = None   # GEMM workspace, grown on demand
 
     def calibrate(self, X):
         """NVFP4 only: per-tensor activation scale from calibration activations (device tensor)."""
@@ -68,7 +69,12 @@ class W4A4Layer:
         W.wush_transform_quant(self.fmt, X, self.Tx, codes, scales, g=self.x_g)
 
     def matmul(self, codes, scales, Y):
-        W.wush_w4a4_gemm(self.fmt, codes, scales, self.w_codes, self.w_scales, Y, a_g=self.x_g, b_g=self.w_g)
+        n = codes.shape[0]
+        need = W.wush_w4a4_gemm_ws_bytes(self.fmt, n, self.d_out, self.d_in)
+        if need and (self._ws is None or self._ws.numel() < need or self._ws.device != codes.device):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=codes.device)
+        W.wush_w4a4_gemm(self.fmt, codes, scales, self.w_codes, self.w_scales, Y, a_g=self.x_g, b_g=self.w_g,
+                         ws=self._ws if need else None)
 
     def forward(self, X, out=None):
         n = X.shape[0]

@@ -102,6 +102,8 @@ class Layer:
         self.xc = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device=dev)
         self.xsc = torch.empty((self.M, nblk), dtype=sdt, device=dev)
         self.Y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
+        wsb = W.wush_w4a4_gemm_ws_bytes(fmt, self.M, self.N, self.K)
+        self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev) if wsb else None
         self.x_elem_bytes = 2 if wl.dtype == "bf16" else 4
         self.host = (Wt, X, Tx, Tw)
         self.setup_s = time.time() - t0
@@ -136,7 +138,7 @@ def run_layer_steps(layers, W, torch, steps, warmup, rotate):
             W.wush_transform_quant(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
             if ev is not None:
                 ev[li][1].record(stream)
-            W.wush_w4a4_gemm(L.fmt, L.xc, L.xsc, L.wc[r], L.wsc[r], L.Y, a_g=L.x_g, b_g=L.w_g)
+            W.wush_w4a4_gemm(L.fmt, L.xc, L.xsc, L.wc[r], L.wsc[r], L.Y, a_g=L.x_g, b_g=L.w_g, ws=L.ws)
             if ev is not None:
                 ev[li][2].record(stream)
 
@@ -370,14 +372,15 @@ def bench_had256(args, W, torch):
     P = [planes] + [planes.clone() for _ in range(args.rotate - 1)]
     S = [sc] + [sc.clone() for _ in range(args.rotate - 1)]
     y = torch.empty((B, d_out), dtype=torch.float32, device=dev)
+    ws = torch.empty(W.wush_had256_gemv_ws_bytes(B, d_in), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        W.wush_had256_gemv(xd, P[i % args.rotate], S[i % args.rotate], y)
+        W.wush_had256_gemv(xd, P[i % args.rotate], S[i % args.rotate], y, ws=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        W.wush_had256_gemv(xd, P[i % args.rotate], S[i % args.rotate], y)
+        W.wush_had256_gemv(xd, P[i % args.rotate], S[i % args.rotate], y, ws=ws)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps

@@ -156,19 +156,24 @@ wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float*
  *   A: a_codes [M][K/2], a_scales [M][K/bs]  (activations, from wush_transform_quant)
  *   B: b_codes [N][K/2], b_scales [N][K/bs]  (weights, from wush_pack_weights)
  *   Y: device out, [M][N] fp32.
- * MXFP4 runs on the gfx950 block-scaled FP4 matrix cores; NVFP4 and INT4 use
- * exact dequantization to bf16 / int8 matrix cores with per-block scaling.
- * Asynchronous on `stream`.  For MXFP4 with K >= 256 the call takes
- * (ceil(M/256) + ceil(N/256)) * ceil(K/256) * 2048 bytes of stream-ordered
- * scratch (hipMallocAsync / hipFreeAsync on `stream`, from the device's
- * default memory pool) for the scales re-laid in the kernel's order; the
- * caller's buffers are only read (A, B) or written (Y).
- * Errors: WUSH_E_ARG, WUSH_E_SHAPE (M, N < 1; K < 1 or K % 128), WUSH_E_HIP
- * (launch failure, or the scratch could not be allocated). */
+ *   ws: device scratch of at least wush_w4a4_gemm_ws_bytes(fmt, M, N, K)
+ *       bytes (16-byte aligned), used only during the call (stream order);
+ *       calls that share a ws must be ordered on one stream.  ws = NULL makes
+ *       the call take the scratch itself from the device's default memory pool
+ *       (hipMallocAsync / hipFreeAsync on `stream`), which costs several
+ *       microseconds per call.
+ * MXFP4 runs on the gfx950 block-scaled FP4 matrix cores (K >= 256 first
+ * re-lays the scales, in ws, in the order the kernel stages them); NVFP4 and
+ * INT4 use exact dequantization to bf16 / int8 matrix cores with per-block
+ * scaling.  Asynchronous on `stream`; A and B are only read.
+ * Errors: WUSH_E_ARG (null or misaligned pointers, ws_bytes too small),
+ * WUSH_E_SHAPE (M, N < 1; K < 1 or K % 128), WUSH_E_HIP (launch failure, or no
+ * scratch from the pool). */
+size_t wush_w4a4_gemm_ws_bytes(wush_format fmt, int M, int N, int K);
 wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K,
                            const uint8_t* a_codes, const void* a_scales, float a_g,
                            const uint8_t* b_codes, const void* b_scales, float b_g,
-                           float* Y, void* stream);
+                           float* Y, void* ws, size_t ws_bytes, void* stream);
 
 /* Layer loss of [WUSH-radio] "Problem Setup and Goal":
  *   *loss = sum over M x N of (Yhat - Yref)^2 / (M * N), accumulated in fp64
@@ -197,12 +202,20 @@ wush_status wush_had256_pack_weights(int d_out, int d_in, const float* W,
                                      uint8_t* planes, uint16_t* scales, void* stream);
 
 /* y[b][j] = sum_k x[b][k] * w_hat[j][k] with w_hat = s16 * (H_256 q) / 16 per
- * 256-vector (the inverse rotation of the dequantized codes).
+ * 256-vector (the inverse rotation of the dequantized codes).  Computed as
+ * (s16/16) sum_m q_m (H_256 x)_m per vector (H_256 is symmetric), with the
+ * rotated activations split into two int8 terms per 256-chunk (relative error
+ * below 2^-15 of the chunk's largest value) and exact int32 dot products.
  *   x       device, [batch][d_in] bf16 bits.   y  device out, [batch][d_out] fp32.
+ *   ws      device scratch of at least wush_had256_gemv_ws_bytes(batch, d_in)
+ *           bytes (16-byte aligned), or NULL (taken from the default memory
+ *           pool per call, as for wush_w4a4_gemm); calls sharing a ws must be
+ *           ordered on one stream.
  * Errors: WUSH_E_SHAPE (batch not in 1..16, d_in % 256), WUSH_E_ARG, WUSH_E_HIP. */
+size_t wush_had256_gemv_ws_bytes(int batch, int d_in);
 wush_status wush_had256_gemv(int batch, int d_out, int d_in, const uint16_t* x,
                              const uint8_t* planes, const uint16_t* scales,
-                             float* y, void* stream);
+                             float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Unquantized rotation v = H_256 w / 16 per 256-vector, in place allowed
  * (in == out).  H/16 is orthogonal and its own inverse, so two calls return

@@ -47,11 +47,17 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert L.wush_transform_quant(0, 0, 4, 63, None, None, 0.0, None, None, None) == W.WUSH_E_SHAPE
     assert L.wush_transform_quant(9, 0, 4, 64, None, None, 0.0, None, None, None) == W.WUSH_E_ARG
     assert b"format" in L.wush_last_error()
-    assert L.wush_w4a4_gemm(0, 4, 4, 100, None, None, 1.0, None, None, 1.0, None, None) == W.WUSH_E_SHAPE
-    assert L.wush_w4a4_gemm(0, 4, 4, 128, None, None, 1.0, None, None, 1.0, None, None) == W.WUSH_E_ARG
-    assert L.wush_w4a4_gemm(0, 0, 4, 128, None, None, 1.0, None, None, 1.0, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_w4a4_gemm(0, 4, 4, 100, None, None, 1.0, None, None, 1.0, None, None, 0, None) == W.WUSH_E_SHAPE
+    assert L.wush_w4a4_gemm(0, 4, 4, 128, None, None, 1.0, None, None, 1.0, None, None, 0, None) == W.WUSH_E_ARG
+    assert L.wush_w4a4_gemm(0, 0, 4, 128, None, None, 1.0, None, None, 1.0, None, None, 0, None) == W.WUSH_E_SHAPE
     assert L.wush_layer_loss(0, 4, None, None, None, None, None) == W.WUSH_E_ARG
-    assert L.wush_had256_gemv(17, 4, 256, None, None, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_had256_gemv(17, 4, 256, None, None, None, None, None, 0, None) == W.WUSH_E_SHAPE
+    # workspace sizes (host-side arithmetic only)
+    assert L.wush_had256_gemv_ws_bytes(4, 4096) == 2 * 4 * 4096 + 4 * 16 * 4
+    assert L.wush_had256_gemv_ws_bytes(0, 4096) == 0
+    assert L.wush_w4a4_gemm_ws_bytes(0, 4096, 12288, 4096) == (16 + 48) * 16 * 2048
+    assert L.wush_w4a4_gemm_ws_bytes(0, 4096, 12288, 128) == 0
+    assert L.wush_w4a4_gemm_ws_bytes(1, 4096, 12288, 4096) == 0
     assert L.wush_had256_pack_weights(4, 100, None, None, None, None) == W.WUSH_E_SHAPE
     assert L.wush_had256_rotate(4, 256, None, None, None) == W.WUSH_E_ARG
     assert L.wush_loss_ws_bytes(10, 10) >= 8

@@ -157,12 +157,29 @@ def test_w4a4_gemm(fmt, shape):
     M, N, K = shape
     ca, sa, cb, sb, ga, gb = _rand_operands(fmt, M, N, K, 1)
     ref = og.w4a4_gemm(fmt, ca, sa, cb, sb, ga, gb)
-    Y = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
-    W.wush_w4a4_gemm(fmt, to_dev(ca), to_dev(sa), to_dev(cb), to_dev(sb), Y,
-                     a_g=ga or 1.0, b_g=gb or 1.0)
-    torch.cuda.synchronize()
-    ok, worst = gemm_close(host(Y), ref)
-    assert ok, (fmt, shape, worst)
+    # both scratch paths: library-taken (ws None) and a caller workspace filled with junk
+    need = W.wush_w4a4_gemm_ws_bytes(fmt, M, N, K)
+    ws = torch.full((need + 64,), 0xA5, dtype=torch.uint8, device=DEV) if need else None
+    for w in (None, ws):
+        Y = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+        W.wush_w4a4_gemm(fmt, to_dev(ca), to_dev(sa), to_dev(cb), to_dev(sb), Y,
+                         a_g=ga or 1.0, b_g=gb or 1.0, ws=w)
+        torch.cuda.synchronize()
+        ok, worst = gemm_close(host(Y), ref)
+        assert ok, (fmt, shape, w is None, worst)
+
+
+def test_w4a4_gemm_workspace_checks():
+    M, N, K = 300, 260, 512
+    ca, sa, cb, sb, _, _ = _rand_operands("mxfp4", M, N, K, 2)
+    need = W.wush_w4a4_gemm_ws_bytes("mxfp4", M, N, K)
+    assert need == (2 + 2) * 2 * 2048            # (row tiles of A + of B) x K blocks x 2 KB
+    assert W.wush_w4a4_gemm_ws_bytes("mxfp4", M, N, 128) == 0   # K = 128: direct kernel, no scratch
+    assert W.wush_w4a4_gemm_ws_bytes("nvfp4", M, N, K) == 0
+    Y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(W.WushError):
+        W.wush_w4a4_gemm("mxfp4", to_dev(ca), to_dev(sa), to_dev(cb), to_dev(sb), Y, ws=small)
 
 
 def test_layer_loss():
@@ -205,16 +222,21 @@ def test_had256_pack_bit_exact_and_rotate():
     assert np.array_equal(host(a), ints)
 
 
-@pytest.mark.parametrize("batch", [1, 3, 4, 5, 16])
-def test_had256_gemv(batch):
-    Wt, _ = random_case(31, 1, 1280, 200)
+# d_in 1280 = 5 chunks (one partial pass of the 16-chunk staging), 5120 = 20
+# chunks (a full pass plus a partial one); d_out 200 leaves a ragged row tile
+@pytest.mark.parametrize("batch,d_in", [(1, 1280), (3, 1280), (4, 1280), (5, 1280), (16, 1280), (1, 5120),
+                                        (16, 5120)])
+def test_had256_gemv(batch, d_in):
+    Wt, _ = random_case(31, 1, d_in, 200)
     rp, rs = oh.pack_weights(Wt)
-    x = np.random.default_rng(batch).standard_normal((batch, 1280)).astype(np.float32)
+    x = np.random.default_rng(batch).standard_normal((batch, d_in)).astype(np.float32)
     from synth.gen import bf16_round, bf16_bits
     xb = bf16_round(x)
     ref = oh.gemv(xb, rp, rs)
-    y = torch.full((batch, 200), np.nan, dtype=torch.float32, device=DEV)
-    W.wush_had256_gemv(to_dev(bf16_bits(xb).view(np.int16)), to_dev(rp), to_dev(rs.view(np.int16)), y)
-    torch.cuda.synchronize()
-    ok, worst = gemm_close(host(y), ref)
-    assert ok, worst
+    ws = torch.full((W.wush_had256_gemv_ws_bytes(batch, d_in),), 0x5A, dtype=torch.uint8, device=DEV)
+    for w in (None, ws):
+        y = torch.full((batch, 200), np.nan, dtype=torch.float32, device=DEV)
+        W.wush_had256_gemv(to_dev(bf16_bits(xb).view(np.int16)), to_dev(rp), to_dev(rs.view(np.int16)), y, ws=w)
+        torch.cuda.synchronize()
+        ok, worst = gemm_close(host(y), ref)
+        assert ok, (w is None, worst)
