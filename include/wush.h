@@ -163,9 +163,12 @@ wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float*
  *       (hipMallocAsync / hipFreeAsync on `stream`), which costs several
  *       microseconds per call.
  * MXFP4 runs on the gfx950 block-scaled FP4 matrix cores (K >= 256 first
- * re-lays the scales, in ws, in the order the kernel stages them); NVFP4 and
- * INT4 use exact dequantization to bf16 / int8 matrix cores with per-block
- * scaling.  Asynchronous on `stream`; A and B are only read.
+ * re-lays the scales, in ws, in the order the kernel stages them).  NVFP4
+ * dequantizes exactly to fp16 (every E2M1 x E4M3 product is an fp16 number)
+ * on the fp16 matrix cores, its block scales likewise re-laid in ws first.
+ * INT4 runs one exact int8 matrix product per 32-group with an fp32 rescale.
+ * The workspace size is 0 where a path needs none.  Asynchronous on
+ * `stream`; A and B are only read.
  * Errors: WUSH_E_ARG (null or misaligned pointers, ws_bytes too small),
  * WUSH_E_SHAPE (M, N < 1; K < 1 or K % 128), WUSH_E_HIP (launch failure, or no
  * scratch from the pool). */
