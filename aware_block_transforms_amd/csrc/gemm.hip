@@ -18,14 +18,16 @@ wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA,
 size_t gemm_nvfp4_ws_bytes(int M, int N, int K);
 wush_status gemm_nvfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, float ga, const uint8_t* B,
                        const uint8_t* SB, float gb, float* Y, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t gemm_int4_ws_bytes(int M, int N, int K);
 wush_status gemm_int4(int M, int N, int K, const uint8_t* A, const uint16_t* SA, const uint8_t* B,
-                      const uint16_t* SB, float* Y, hipStream_t stream);
+                      const uint16_t* SB, float* Y, void* ws, size_t ws_bytes, hipStream_t stream);
 }  // namespace wush
 
 extern "C" size_t wush_w4a4_gemm_ws_bytes(wush_format fmt, int M, int N, int K) {
   if (M < 1 || N < 1 || K < 128 || K % 128) return 0;
   if (fmt == WUSH_MXFP4) return wush::gemm_mxfp4_ws_bytes(M, N, K);
   if (fmt == WUSH_NVFP4) return wush::gemm_nvfp4_ws_bytes(M, N, K);
+  if (fmt == WUSH_INT4) return wush::gemm_int4_ws_bytes(M, N, K);
   return 0;
 }
 
@@ -53,7 +55,7 @@ extern "C" wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K, cons
                               static_cast<const uint8_t*>(b_scales), b_g, Y, ws, ws_bytes, s);
     case WUSH_INT4:
       return wush::gemm_int4(M, N, K, a_codes, static_cast<const uint16_t*>(a_scales), b_codes,
-                             static_cast<const uint16_t*>(b_scales), Y, s);
+                             static_cast<const uint16_t*>(b_scales), Y, ws, ws_bytes, s);
   }
   return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: bad format");
 }

@@ -235,8 +235,10 @@ wush_status gemm_nvfp4_direct(int M, int N, int K, const uint8_t* A, const uint8
   return WUSH_OK;
 }
 
-wush_status gemm_int4(int M, int N, int K, const uint8_t* A, const uint16_t* SA, const uint8_t* B, const uint16_t* SB,
-                      float* Y, hipStream_t stream) {
+// Direct-load kernel: operands of 2^31 bytes or more (beyond the LDS kernel's
+// 32-bit buffer offsets).
+wush_status gemm_int4_direct(int M, int N, int K, const uint8_t* A, const uint16_t* SA, const uint8_t* B,
+                             const uint16_t* SB, float* Y, hipStream_t stream) {
   dim3 grid((N + kBlockN - 1) / kBlockN, (M + kBlockM - 1) / kBlockM);
   if (grid.y > 65535u) return fail(WUSH_E_SHAPE, "wush_w4a4_gemm: M too large");
   hipLaunchKernelGGL(gemm_int4_kernel, grid, dim3(256), 0, stream, A, SA, B, SB, Y, M, N, K);

@@ -166,8 +166,10 @@ wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float*
  * re-lays the scales, in ws, in the order the kernel stages them).  NVFP4
  * dequantizes exactly to fp16 (every E2M1 x E4M3 product is an fp16 number)
  * on the fp16 matrix cores, its block scales likewise re-laid in ws first.
- * INT4 runs one exact int8 matrix product per 32-group with an fp32 rescale.
- * The workspace size is 0 where a path needs none.  Asynchronous on
+ * INT4 runs one exact int8 matrix product per 32-group with an fp32 rescale,
+ * its scales re-laid as fp32 in ws first.  The workspace size is 0 where a
+ * path needs none (operands of 2^31 bytes or more take slower direct-load
+ * kernels without scratch).  Asynchronous on
  * `stream`; A and B are only read.
  * Errors: WUSH_E_ARG (null or misaligned pointers, ws_bytes too small),
  * WUSH_E_SHAPE (M, N < 1; K < 1 or K % 128), WUSH_E_HIP (launch failure, or no

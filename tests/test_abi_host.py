@@ -59,7 +59,7 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert L.wush_w4a4_gemm_ws_bytes(0, 4096, 12288, 128) == 0
     assert L.wush_w4a4_gemm_ws_bytes(1, 4096, 12288, 4096) == (16 + 48) * 16 * 8192
     assert L.wush_w4a4_gemm_ws_bytes(1, 4096, 12288, 128) == (16 + 48) * 1 * 8192
-    assert L.wush_w4a4_gemm_ws_bytes(2, 4096, 12288, 4096) == 0
+    assert L.wush_w4a4_gemm_ws_bytes(2, 4096, 12288, 4096) == 16 * (16 * 8192 + 96 * 4096)
     assert L.wush_had256_pack_weights(4, 100, None, None, None, None) == W.WUSH_E_SHAPE
     assert L.wush_had256_rotate(4, 256, None, None, None) == W.WUSH_E_ARG
     assert L.wush_loss_ws_bytes(10, 10) >= 8

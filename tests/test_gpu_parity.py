@@ -177,7 +177,8 @@ def test_w4a4_gemm_workspace_checks():
     assert W.wush_w4a4_gemm_ws_bytes("mxfp4", M, N, 128) == 0   # K = 128: direct kernel, no scratch
     # NVFP4: 16 fp16 scale planes of 256 entries per (row tile, K block)
     assert W.wush_w4a4_gemm_ws_bytes("nvfp4", M, N, K) == (2 + 2) * 2 * 8192
-    assert W.wush_w4a4_gemm_ws_bytes("int4", M, N, K) == 0
+    # INT4: fp32 scales, 8 per row and K block (256-row A tiles, 128-row B tiles)
+    assert W.wush_w4a4_gemm_ws_bytes("int4", M, N, K) == 2 * (2 * 8192 + 3 * 4096)
     Y = torch.empty((M, N), dtype=torch.float32, device=DEV)
     small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
     with pytest.raises(W.WushError):
@@ -186,6 +187,10 @@ def test_w4a4_gemm_workspace_checks():
     small = torch.empty(W.wush_w4a4_gemm_ws_bytes("nvfp4", M, N, K) - 16, dtype=torch.uint8, device=DEV)
     with pytest.raises(W.WushError):
         W.wush_w4a4_gemm("nvfp4", to_dev(ca), to_dev(sa), to_dev(cb), to_dev(sb), Y, a_g=ga, b_g=gb, ws=small)
+    ca, sa, cb, sb, _, _ = _rand_operands("int4", M, N, K, 2)
+    small = torch.empty(W.wush_w4a4_gemm_ws_bytes("int4", M, N, K) - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(W.WushError):
+        W.wush_w4a4_gemm("int4", to_dev(ca), to_dev(sa), to_dev(cb), to_dev(sb), Y, ws=small)
 
 
 def test_layer_loss():
