@@ -57,7 +57,9 @@ __device__ __forceinline__ v4i make_desc(const void* base, uint32_t bytes) {
 // lds; lds is wave-uniform).  Written as asm so that the compiler does not
 // treat it as an LDS store and make every later LDS read wait for all DMA in
 // flight; the kernel orders the two itself (s_waitcnt vmcnt(0) and a barrier
-// before LDS written by DMA is read).  The instruction writes no register.
+// before LDS written by DMA is read).  The instruction writes no register
+// except M0, which nothing else in these kernels reads (a CPU test checks the
+// compiled code).
 __device__ __forceinline__ void dma16(const v4i& desc, const void* lds, uint32_t voff, uint32_t soff) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"

@@ -33,10 +33,14 @@ if ROOT not in sys.path:
 # MI355X published peaks
 HBM_GBPS = 8000.0
 MXFP4_TFLOPS = 10100.0      # dense FP4 matrix
-BF16_TFLOPS = 2500.0        # dense bf16 matrix (NVFP4 path)
-INT8_TOPS = 5000.0          # dense int8 matrix (INT4 path)
+FP16_TFLOPS = 2500.0        # dense fp16 matrix (NVFP4 path)
+INT8_TOPS = 5000.0          # dense int8 matrix
 # fp32 FMA on the vector ALU without packed math: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
 VALU_FP32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# vector-ALU lane operations: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# INT4 matmul: per output and 32-group, convert + multiply + fma on the vector ALU
+INT4_RESCALE_OPS = 3
 
 METRIC = "W4A4 layer TFLOPS (transform+quant+GEMM) & quant GB/s, % roofline"
 
@@ -303,7 +307,7 @@ def main():
     tq_flops = sum(L.tq_flops() for L in layers)
     tq_t = sum(tq_ms) / 1e3
     gm_t = sum(gm_ms) / 1e3
-    gemm_peak = {"mxfp4": MXFP4_TFLOPS, "nvfp4": BF16_TFLOPS, "int4": INT8_TOPS}[fmt]
+    gemm_peak = {"mxfp4": MXFP4_TFLOPS, "nvfp4": FP16_TFLOPS, "int4": INT8_TOPS}[fmt]
     gemm_achieved = flops / gm_t / 1e12
     tq_alu = tq_flops / tq_t / 1e12
     tq_gbps = tq_bytes / tq_t / 1e9
@@ -316,6 +320,12 @@ def main():
                  "traffic": measured_traffic("wush_w4a4_gemm", wname) if fmt == "mxfp4" else None,
                  "algorithmic_bytes": round(sum(L.gemm_bytes() for L in layers) / len(layers)),
                  "avg_us": round(gm_t * 1e6 / len(layers), 2)}
+    if fmt == "int4":
+        # the per-group fp32 rescale on the vector ALU bounds the INT4 matmul
+        rescale = sum(INT4_RESCALE_OPS * L.M * L.N * (L.K // 32) for L in layers) / gm_t / 1e12
+        roof_gemm.update({"bound": "alu", "achieved": round(rescale, 2), "peak": round(VALU_TOPS, 1),
+                          "unit": "Top/s", "frac": round(rescale / VALU_TOPS, 4),
+                          "int8_TOPS": round(gemm_achieved, 2), "int8_frac": round(gemm_achieved / INT8_TOPS, 4)})
     t_alu = tq_flops / (VALU_FP32_TFLOPS * 1e12)
     t_hbm = tq_bytes / (HBM_GBPS * 1e9)
     if t_alu > t_hbm:

@@ -157,3 +157,26 @@ def test_builder_on_tiny_workload():
     W.wush_build_transforms("wush", 32, Wt, Sx, Tx, Tw)
     rx, rw, _, _ = tr.build_transforms("wush", Wt, tr.activation_moments(X, 32).astype(np.float32), 32)
     assert np.all(np.abs(Tx - rx) <= _t_tolerance(Tx, rx) + 4 * 2.0 ** -24 * np.abs(rx).max())
+
+
+def test_dma_kernels_leave_m0_to_their_dma():
+    """The NVFP4 and INT4 kernels set M0 in inline asm just before each
+    buffer_load ... lds (the compiler cannot see that write); no other
+    instruction of theirs may read or write M0."""
+    import re
+    import subprocess
+    from aware_block_transforms_amd import build as B
+    for src in ("gemm_nvfp4.hip", "gemm_int4.hip"):
+        r = subprocess.run([B.HIPCC, *B.HIP_FLAGS, "--cuda-device-only", "-S", "-o", "-",
+                            os.path.join(B.CSRC, src)], capture_output=True, text=True, timeout=600)
+        assert r.returncode == 0, r.stderr[-2000:]
+        lines = [l.strip() for l in r.stdout.splitlines()]
+        code = [l for l in lines if l and not l.startswith((";", ".", "//")) and "ASM" not in l]
+        n_dma = 0
+        for i, l in enumerate(code):
+            if not re.search(r"\bm0\b", l):
+                continue
+            assert re.match(r"s_mov_b32 m0, s\d+$", l), (src, l)
+            assert re.match(r"buffer_load_dwordx4 .* offen lds$", code[i + 1]), (src, l, code[i + 1])
+            n_dma += 1
+        assert n_dma > 0, src
