@@ -48,9 +48,10 @@ _SIGS = {
     "wush_w4a4_gemm": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _f, _p, _p, _sz, _p], _i),
     "wush_layer_loss": ([_i, _i, _p, _p, _p, _p, _p], _i),
     "wush_loss_ws_bytes": ([_i, _i], _sz),
-    "wush_had256_pack_weights": ([_i, _i, _p, _p, _p, _p], _i),
+    "wush_had256_packed_bytes": ([_i, _i], _sz),
+    "wush_had256_pack_weights": ([_i, _i, _p, _p, _p], _i),
     "wush_had256_gemv_ws_bytes": ([_i, _i], _sz),
-    "wush_had256_gemv": ([_i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
+    "wush_had256_gemv": ([_i, _i, _i, _p, _p, _p, _p, _sz, _p], _i),
     "wush_had256_rotate": ([_i, _i, _p, _p, _p], _i),
     "wush_status_string": ([_i], ctypes.c_char_p),
     "wush_last_error": ([], ctypes.c_char_p),
@@ -175,9 +176,20 @@ def wush_layer_loss(Yhat, Yref, loss, ws, stream=None):
            "wush_layer_loss")
 
 
-def wush_had256_pack_weights(W, planes, scales, stream=None):
+def wush_had256_packed_bytes(d_out, d_in):
+    return lib.wush_had256_packed_bytes(d_out, d_in)
+
+
+def _packed_check(packed, d_out, d_in, name):
+    need = lib.wush_had256_packed_bytes(d_out, d_in)
+    if packed.numel() * packed.element_size() < need:
+        raise ValueError("%s: packed buffer of %d bytes, need %d" % (name, packed.numel() * packed.element_size(), need))
+
+
+def wush_had256_pack_weights(W, packed, stream=None):
     d_out, d_in = W.shape
-    _check(lib.wush_had256_pack_weights(d_out, d_in, _ptr(W), _ptr(planes), _ptr(scales), _stream(stream)),
+    _packed_check(packed, d_out, d_in, "wush_had256_pack_weights")
+    _check(lib.wush_had256_pack_weights(d_out, d_in, _ptr(W), _ptr(packed), _stream(stream)),
            "wush_had256_pack_weights")
 
 
@@ -185,12 +197,13 @@ def wush_had256_gemv_ws_bytes(batch, d_in):
     return lib.wush_had256_gemv_ws_bytes(batch, d_in)
 
 
-def wush_had256_gemv(x, planes, scales, y, ws=None, stream=None):
+def wush_had256_gemv(x, packed, y, ws=None, stream=None):
     batch, d_in = x.shape
     d_out = y.shape[1]
+    _packed_check(packed, d_out, d_in, "wush_had256_gemv")
     wp, wb = _ws(ws)
-    _check(lib.wush_had256_gemv(batch, d_out, d_in, _ptr(x), _ptr(planes), _ptr(scales), _ptr(y), wp, wb,
-                                _stream(stream)), "wush_had256_gemv")
+    _check(lib.wush_had256_gemv(batch, d_out, d_in, _ptr(x), _ptr(packed), _ptr(y), wp, wb, _stream(stream)),
+           "wush_had256_gemv")
 
 
 def wush_had256_rotate(inp, out, stream=None):

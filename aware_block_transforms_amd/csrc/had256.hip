@@ -8,14 +8,21 @@
 //
 // Pack: one workgroup of 256 threads per 256-vector; the 8 butterfly stages
 // run through LDS in the pinned order (h = 1, 2, ..., 128), then x 1/16, the
-// vector maximum, an fp16 scale and codes in [-3, 3] stored as two bit planes.
+// vector maximum, an fp16 scale and codes q in [-3, 3].  The codes are stored
+// as c = q + 4 in records of 16 rows x 256 codes laid out for the GEMV's
+// loads: per (16-row block, chunk) 1568 bytes = 64 lanes x 16 bytes of code
+// bits 0-1, 64 lanes x 8 bytes of code bit 2, and the 16 fp16 scales.  Lane
+// l = 16 g + r holds row r's codes 64 g .. 64 g + 63; byte m of its 16 holds
+// codes 64 g + 16 t + m (t = 0..3) at bits 2 t, and byte 4 j + b of its 8
+// holds bit 2 of code 64 g + 16 (u / 2) + 8 j + 4 (u % 2) + b at bit u.
 //
 // GEMV: instead of inverse-rotating every weight (8 butterflies per weight on
 // the vector ALU), the rotation is moved to the activations, which every
 // output row shares:  sum_k x_k * (s/16)(H q)_k = (s/16) * sum_m q_m (H x)_m
-// because H is symmetric.  A pre-pass rotates each activation chunk once and
-// splits it into two int8 terms; the weight stream then only unpacks codes to
-// int8 (byte permutes) and the dot products run on the int8 matrix cores.
+// because H is symmetric.  The activations of each chunk are rotated once and
+// split into two int8 terms; the weight stream then only unpacks codes to
+// int8 (a shift and a masked merge per 4 codes) and the dot products run on
+// the int8 matrix cores.
 
 #include <hip/hip_runtime.h>
 
@@ -26,7 +33,10 @@
 namespace {
 
 constexpr int kVec = 256;
-constexpr int kBytes = 96;
+constexpr int kBlockRows = 16;
+constexpr int kRecord = 1568;      // per (16-row block, chunk)
+constexpr int kHiPlane = 1024;     // offset of the bit-2 plane in a record
+constexpr int kScales = 1536;      // offset of the 16 fp16 scales
 
 // In-place forward FWHT of a 256-vector held one element per thread in `v`
 // (LDS).  Thread t returns its element after all 8 stages.
@@ -46,17 +56,18 @@ __device__ __forceinline__ float fwht256_lds(float* v, float val) {
   return v[t];
 }
 
-__global__ __launch_bounds__(kVec) void had256_pack_kernel(const float* __restrict__ W, int d_in,
-                                                           uint8_t* __restrict__ planes,
-                                                           uint16_t* __restrict__ scales) {
+// One workgroup per (row, chunk) over the rows padded to a multiple of 16;
+// padding rows are zero vectors (codes q = 0, scale 0).
+__global__ __launch_bounds__(kVec) void had256_pack_kernel(const float* __restrict__ W, int d_out, int d_in,
+                                                           uint8_t* __restrict__ packed) {
   __shared__ float v[kVec];
   __shared__ uint32_t wmax[kVec / 64];
   __shared__ uint8_t cc[kVec];
   const int t = threadIdx.x;
   const int nv = d_in / kVec;
   const size_t vec = blockIdx.x;                 // row * nv + chunk
-  const size_t row = vec / nv, c = vec % nv;
-  const float x = W[row * d_in + c * kVec + t];
+  const int row = static_cast<int>(vec / nv), c = static_cast<int>(vec % nv);
+  const float x = (row < d_out) ? W[static_cast<size_t>(row) * d_in + c * kVec + t] : 0.0f;
   const float r0 = fwht256_lds(v, x) * 0.0625f;
   uint32_t ab = __float_as_uint(r0) & 0x7fffffffu;
 #pragma unroll
@@ -72,23 +83,29 @@ __global__ __launch_bounds__(kVec) void had256_pack_kernel(const float* __restri
     const float r = 1.0f / s32;
     q = static_cast<int>(fminf(fmaxf(rintf(r0 * r), -3.0f), 3.0f));
   }
-  cc[t] = static_cast<uint8_t>(q & 7);
+  cc[t] = static_cast<uint8_t>(q + 4);
   __syncthreads();
-  uint8_t* dst = planes + vec * kBytes;
+  const int r = row % kBlockRows;
+  uint8_t* rec = packed + (static_cast<size_t>(row / kBlockRows) * nv + c) * kRecord;
   if (t < 64) {
-    dst[t] = static_cast<uint8_t>((cc[4 * t] & 3) | ((cc[4 * t + 1] & 3) << 2) | ((cc[4 * t + 2] & 3) << 4) |
-                                  ((cc[4 * t + 3] & 3) << 6));
-  } else if (t < 96) {
-    const int j = t - 64;
-    uint32_t b = 0;
+    // bits 0-1: lane 16 g + r, byte m
+    const int g = t >> 4, m = t & 15;
+    uint32_t byte = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) b |= ((cc[8 * j + i] >> 2) & 1u) << i;
-    dst[t] = static_cast<uint8_t>(b);
+    for (int tt = 0; tt < 4; ++tt) byte |= (cc[64 * g + 16 * tt + m] & 3u) << (2 * tt);
+    rec[16 * (16 * g + r) + m] = static_cast<uint8_t>(byte);
+  } else if (t < 96) {
+    // bit 2: lane 16 g + r, byte 4 j + b
+    const int i = t - 64, g = i >> 3, hb = i & 7, j = hb >> 2, b = hb & 3;
+    uint32_t byte = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) byte |= ((cc[64 * g + 16 * (u >> 1) + 8 * j + 4 * (u & 1) + b] >> 2) & 1u) << u;
+    rec[kHiPlane + 8 * (16 * g + r) + hb] = static_cast<uint8_t>(byte);
   }
   if (t == 0) {
     uint16_t hb;
     __builtin_memcpy(&hb, &h, 2);
-    scales[vec] = hb;
+    *reinterpret_cast<uint16_t*>(rec + kScales + 2 * r) = hb;
   }
 }
 
@@ -113,180 +130,275 @@ __global__ __launch_bounds__(kVec) void had256_rotate_kernel(const float* __rest
 // sigma - a_hi) * 128); the dropped part is below sigma / 256 per element.
 // Then per weight row and chunk
 //   sum_m q_m v_m ~ sigma * (sum_m q_m a_hi_m + (sum_m q_m a_lo_m) / 128)
-// with both sums exact in int32 (v_mfma_i32_16x16x64_i8), and
+// with both sums exact in int32 (v_mfma_i32_16x16x64_i8 on the stored codes
+// c = q + 4, the accumulators starting at -4 sum_m a_m), and
 //   y[b][row] = sum_c (s / 16) * that, accumulated in fp32.
 //
-// K order.  The codes of a chunk are visited in an order that makes the
-// 3-bit unpack cheap: lane group g (of the MFMA's four) owns codes 64 g ..
-// 64 g + 63, i.e. bytes 16 g .. 16 g + 15 of the 2-bit plane and 64 + 8 g ..
-// 64 + 8 g + 7 of the 1-bit plane (one 16-byte and one 8-byte load), and each
-// int8 dword holds the codes 8 j + r of four consecutive octets j for one bit
-// position r, so that both planes yield it with a shift and a mask.  Byte p of
-// the lane's 16 MFMA-t operand bytes holds code
-//   k = 8 (4 (2 g + qq) + jj) + 2 t + rr,  qq = p / 8, rr = (p / 4) % 2, jj = p % 4,
-// and the pre-pass stores the activations in the same order.
+// K order: MFMA t of lane group g takes codes 64 g + 16 t .. + 15 in natural
+// order, so the activation operand of a chunk is its int8 vector as stored.
 
-constexpr int kGemvWaves = 4;      // K split inside a workgroup: wave w takes chunks w, w + 4, ...
-
-// Pre-pass: one workgroup of 256 threads per (chunk, batch row).
-// act: [nv][4 t][4 g][batch][16] int8, a_hi then (at + batch * d_in) a_lo.
-__global__ __launch_bounds__(kVec) void had256_prep_kernel(const uint16_t* __restrict__ x, int batch, int d_in,
-                                                           int8_t* __restrict__ act, float* __restrict__ sig) {
-  __shared__ float v[kVec];
-  __shared__ uint32_t wmax[kVec / 64];
-  const int t = threadIdx.x, c = blockIdx.x, b = blockIdx.y;
-  const int nv = d_in / kVec;
-  const float xv = __uint_as_float(static_cast<uint32_t>(x[static_cast<size_t>(b) * d_in + c * kVec + t]) << 16);
-  const float r = fwht256_lds(v, xv);
-  uint32_t ab = __float_as_uint(r) & 0x7fffffffu;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ab = max(ab, static_cast<uint32_t>(__shfl_xor(static_cast<int>(ab), off)));
-  if ((t & 63) == 0) wmax[t >> 6] = ab;
-  __syncthreads();
-  const float amax = __uint_as_float(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
-  const float sigma = amax / 127.0f;
-  int hi = 0, lo = 0;
-  if (sigma > 0.0f) {
-    const float u = r / sigma;
-    hi = static_cast<int>(fminf(fmaxf(rintf(u), -127.0f), 127.0f));
-    lo = static_cast<int>(fminf(fmaxf(rintf((u - static_cast<float>(hi)) * 128.0f), -127.0f), 127.0f));
-  }
-  // position of code k = t in the operand order described above
-  const int j = t >> 3, rb = t & 7;
-  const int q = j >> 2, jj = j & 3, g = q >> 1, qq = q & 1, tm = rb >> 1, rr = rb & 1;
-  const int p = (2 * qq + rr) * 4 + jj;
-  const size_t o = ((static_cast<size_t>(c * 4 + tm) * 4 + g) * batch + b) * 16 + p;
-  act[o] = static_cast<int8_t>(hi);
-  act[static_cast<size_t>(batch) * d_in + o] = static_cast<int8_t>(lo);
-  if (t == 0) sig[static_cast<size_t>(b) * nv + c] = sigma;
-}
+constexpr int kGemvWaves = 16;     // K split inside a workgroup: wave w takes chunks w, w + 16, ...
+constexpr int kGemvTiles = 4;      // 16-row MFMA tiles (row blocks) per workgroup
+constexpr int kGemvRows = kBlockRows * kGemvTiles;
+constexpr int kFusedBatch = 1;     // batches up to this size rotate their activations inside the GEMV
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// The int8 codes of dword (qq, rr-bit position r) from the lane's plane data.
-// lo_f / hi_f: 2-bit-plane bytes of the four octets (fields of codes 8j+0..3 /
-// 8j+4..7); b2: 1-bit-plane bytes of the same octets.
-__device__ __forceinline__ uint32_t codes4(uint32_t lo_f, uint32_t hi_f, uint32_t b2, int r) {
-  const uint32_t src = (r < 4) ? lo_f : hi_f;
-  const uint32_t l2 = (src >> (2 * (r & 3))) & 0x03030303u;
-  const uint32_t h1 = (b2 >> r) & 0x01010101u;
-  const uint32_t c = l2 | (h1 << 2);                       // 3-bit codes, one per byte
-  return __builtin_amdgcn_perm(0xFFFEFDFCu, 0x03020100u, c);   // -> int8 in [-4, 3]
+// Orders this wave's LDS writes before its later LDS reads of other lanes' data.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Activation operands of chunk c for MFMA t = 0..3 (lane column n = r16 is
-// batch row n; zero past nb), plus sigma.
-__device__ __forceinline__ void load_act(const int8_t* __restrict__ act, const int8_t* __restrict__ act_lo,
-                                         const float* __restrict__ sig, int c, int nv, int nb, int r16, int g,
-                                         v4i (&ah)[4], v4i (&al)[4], float& sg) {
+// Rotated, split activations of one chunk of one batch row.
+struct Split {
+  uint32_t hi, lo;    // the lane's 4 int8 terms of elements 4 L .. 4 L + 3
+  float sigma;
+  int sum_hi, sum_lo; // over the whole chunk
+};
+
+// Rotation and int8 split of one 256-chunk on one wave.  Lane L holds
+// elements 4 L + j, j = 0..3 (bf16 in `xv`).  The butterflies are those of
+// fwht256_lds in the same stage order (h = 1, 2 inside the lane, 4 .. 128
+// across lanes L ^ h/4), so the rotated values are bit-identical to it.
+__device__ __forceinline__ Split rotate_split(const uint2& xv, int lane) {
+  float v[4];
+  const uint32_t xw[2] = {xv.x, xv.y};
 #pragma unroll
-  for (int t = 0; t < 4; ++t) { ah[t] = v4i{0, 0, 0, 0}; al[t] = v4i{0, 0, 0, 0}; }
-  sg = 0.0f;
-  if (r16 < nb && c < nv) {
+  for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(((xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 16);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const size_t o = ((static_cast<size_t>(c * 4 + t) * 4 + g) * nb + r16) * 16;
-      ah[t] = *reinterpret_cast<const v4i*>(act + o);
-      al[t] = *reinterpret_cast<const v4i*>(act_lo + o);
+  for (int h = 1; h < 4; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j & h) continue;
+      const float a = v[j], b = v[j + h];
+      v[j] = a + b;
+      v[j + h] = a - b;
     }
-    sg = sig[static_cast<size_t>(r16) * nv + c];
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float o = __shfl_xor(v[j], m);
+      v[j] = upper ? (o - v[j]) : (v[j] + o);
+    }
+  }
+  uint32_t ab = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ab = max(ab, __float_as_uint(v[j]) & 0x7fffffffu);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) ab = max(ab, static_cast<uint32_t>(__shfl_xor(static_cast<int>(ab), m)));
+  Split sp;
+  sp.sigma = __uint_as_float(ab) / 127.0f;
+  sp.hi = sp.lo = 0;
+  int sh = 0, sl = 0;
+  if (sp.sigma > 0.0f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float u = v[j] / sp.sigma;
+      const int hi = static_cast<int>(fminf(fmaxf(rintf(u), -127.0f), 127.0f));
+      const int lo = static_cast<int>(fminf(fmaxf(rintf((u - static_cast<float>(hi)) * 128.0f), -127.0f), 127.0f));
+      sp.hi |= (static_cast<uint32_t>(hi) & 0xFFu) << (8 * j);
+      sp.lo |= (static_cast<uint32_t>(lo) & 0xFFu) << (8 * j);
+      sh += hi;
+      sl += lo;
+    }
+  }
+  // both sums are within +-256 * 127, so one int32 carries them: 65536 sh + sl
+  int packed = sh * 65536 + sl;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) packed += __shfl_xor(packed, m);
+  sp.sum_lo = static_cast<int>(static_cast<int16_t>(packed & 0xFFFF));
+  sp.sum_hi = (packed - sp.sum_lo) / 65536;
+  return sp;
+}
+
+// Pre-pass for batches above kFusedBatch: one wave per (chunk, batch row).
+// act: [nv][4 t][4 g][batch][16] int8 a_hi (element 64 g + 16 t + p of the
+// chunk at byte p), then (at + batch * d_in) a_lo, so that the operand load of
+// one MFMA t reads 16 bytes per lane from one contiguous span;
+// stats: [batch][nv] {sigma, sum a_hi, sum a_lo, 0} (the sums as int bits).
+__global__ __launch_bounds__(64) void had256_prep_kernel(const uint16_t* __restrict__ x, int batch, int d_in,
+                                                         int8_t* __restrict__ act, float4* __restrict__ stats) {
+  const int lane = threadIdx.x, c = blockIdx.x, b = blockIdx.y;
+  const int nv = d_in / kVec;
+  const uint2 xv = *reinterpret_cast<const uint2*>(x + static_cast<size_t>(b) * d_in + c * kVec + 4 * lane);
+  const Split sp = rotate_split(xv, lane);
+  // lane L holds elements 4 L .. 4 L + 3: g = L / 16, t = (L / 4) % 4, p = 4 (L % 4)
+  const size_t o = ((static_cast<size_t>(c) * 16 + ((lane >> 2) & 3) * 4 + (lane >> 4)) * batch + b) * 16 + 4 * (lane & 3);
+  *reinterpret_cast<uint32_t*>(act + o) = sp.hi;
+  *reinterpret_cast<uint32_t*>(act + static_cast<size_t>(batch) * d_in + o) = sp.lo;
+  if (lane == 0)
+    stats[static_cast<size_t>(b) * nv + c] =
+        make_float4(sp.sigma, __int_as_float(sp.sum_hi), __int_as_float(sp.sum_lo), 0.0f);
+}
+
+// Activation operands of one chunk for MFMA t = 0..3 (lane column n = r16 is
+// batch row n), its sigma and the sums that undo the +4 code offset.
+struct Act {
+  v4i ah[4], al[4];
+  float sg;
+  int sum_hi, sum_lo;
+};
+
+// Lanes past the batch read row nb - 1 instead of zeros; their output columns
+// are never stored.
+__device__ __forceinline__ void load_act(const int8_t* __restrict__ act, const int8_t* __restrict__ act_lo,
+                                         const float4* __restrict__ stats, int c, int nv, int nb, int r16, int g,
+                                         Act& a) {
+  const int n = min(r16, nb - 1);
+  // 32-bit lane offsets: the operand planes are below 2^24 * 16 bytes
+  const uint32_t o = ((static_cast<uint32_t>(c) * 16 + g) * nb + n) * 16;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    a.ah[t] = *reinterpret_cast<const v4i*>(act + (o + 64 * t * nb));
+    a.al[t] = *reinterpret_cast<const v4i*>(act_lo + (o + 64 * t * nb));
+  }
+  const float4 st = stats[static_cast<size_t>(n) * nv + c];
+  a.sg = st.x;
+  a.sum_hi = __float_as_int(st.y);
+  a.sum_lo = __float_as_int(st.z);
+}
+
+// Operand dword i of MFMA t from the lane's record bytes: four stored codes
+// c in [1, 7], bits 0-1 from low-plane dword i at bits 2 t of each byte, bit 2
+// from high-plane dword i / 2 at bit 2 t + i % 2 of each byte.
+template <int t, int i>
+__device__ __forceinline__ int codes4(const uint4& p1, const uint2& p2) {
+  const uint32_t d = (i == 0) ? p1.x : (i == 1) ? p1.y : (i == 2) ? p1.z : p1.w;
+  const uint32_t e = (i < 2) ? p2.x : p2.y;
+  constexpr int u = 2 * t + (i & 1);
+  const uint32_t hb = (u >= 2) ? (e >> (u - 2)) : (e << (2 - u));
+  return static_cast<int>(((d >> (2 * t)) & 0x03030303u) | (hb & 0x04040404u));
+}
+
+template <int t>
+__device__ __forceinline__ v4i codes16(const uint4& p1, const uint2& p2) {
+  return v4i{codes4<t, 0>(p1, p2), codes4<t, 1>(p1, p2), codes4<t, 2>(p1, p2), codes4<t, 3>(p1, p2)};
+}
+
+// One 16-row tile times one chunk; lane (r16, g) gets rows 4 g + e of the
+// tile for batch column r16.  sc holds the rows' fp16 scales; f = sigma /
+// 2048 folds in 1/16 for H and 1/128 for the a_lo weight, so that the exact
+// int32 128 hi + lo (below 2^24, so exact in fp32) times s f is the term.
+__device__ __forceinline__ void tile_dot(const uint4& p1, const uint2& p2, const uint2& sc, const Act& a, float f,
+                                         float (&yp)[4]) {
+  v4i dh = v4i{-4 * a.sum_hi, -4 * a.sum_hi, -4 * a.sum_hi, -4 * a.sum_hi};
+  v4i dl = v4i{-4 * a.sum_lo, -4 * a.sum_lo, -4 * a.sum_lo, -4 * a.sum_lo};
+  {
+    const v4i w = codes16<0>(p1, p2);
+    dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a.ah[0], dh, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a.al[0], dl, 0, 0, 0);
+  }
+  {
+    const v4i w = codes16<1>(p1, p2);
+    dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a.ah[1], dh, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a.al[1], dl, 0, 0, 0);
+  }
+  {
+    const v4i w = codes16<2>(p1, p2);
+    dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a.ah[2], dh, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a.al[2], dl, 0, 0, 0);
+  }
+  {
+    const v4i w = codes16<3>(p1, p2);
+    dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a.ah[3], dh, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a.al[3], dl, 0, 0, 0);
+  }
+  const uint32_t sw[2] = {sc.x, sc.y};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    _Float16 hs;
+    const uint16_t sb = static_cast<uint16_t>(sw[e >> 1] >> (16 * (e & 1)));
+    __builtin_memcpy(&hs, &sb, 2);
+    const int d = dh[e] * 128 + dl[e];
+    yp[e] = fmaf(static_cast<float>(hs) * f, static_cast<float>(d), yp[e]);
   }
 }
 
-// One workgroup = one 16-row tile.  Per pass of up to 16 chunks the tile's
-// packed weights (16 rows x 96 B per chunk, contiguous in HBM) and scales are
-// copied to LDS with full-line loads that are all in flight at once, then
-// wave w takes chunks w, w + 4, ... of the pass out of LDS (rows padded to
-// 1552 bytes: the 16 lanes of one row group hit distinct banks).  The
-// activation operands (L2-resident) are loaded per chunk.
-constexpr int kPassChunks = 16;
-constexpr int kRowPitch = kPassChunks * kBytes + 16;   // 1552
-
-template <int B>
-__global__ __launch_bounds__(64 * kGemvWaves) void had256_gemv_i8_kernel(const int8_t* __restrict__ act,
-                                                                         const float* __restrict__ sig,
-                                                                         const uint8_t* __restrict__ planes,
-                                                                         const uint16_t* __restrict__ scales,
-                                                                         float* __restrict__ y, int nb, int d_out,
-                                                                         int d_in) {
+// One workgroup per 64 output rows (four 16-row blocks), 16 waves.  Wave w
+// takes chunks w, w + 16, ...; per chunk it loads its four records' lane
+// slices straight into registers (16 + 8 contiguous bytes per lane per
+// record, so each load instruction reads one contiguous span) and runs all
+// four tiles against each activation operand, so that an operand fetched
+// once serves 64 rows.  With kFused the wave rotates and splits the chunk's
+// activations itself from bf16 x (through a wave-private LDS slot);
+// otherwise they come from the pre-pass.  The wave partial sums are added in
+// LDS in a fixed order.
+template <int B, bool kFused>
+__global__ __launch_bounds__(64 * kGemvWaves) void had256_gemv_kernel(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ act, const float4* __restrict__ stats,
+    const uint8_t* __restrict__ packed, float* __restrict__ y, int nb, int d_out, int d_in) {
+  static_assert(!kFused || B == 1, "the in-kernel rotation serves one batch row");
   // B is the compiled batch capacity; nb <= B rows of x / y are real.
-  __shared__ __attribute__((aligned(16))) uint8_t wl[16 * kRowPitch];
-  __shared__ uint16_t sl[16 * kPassChunks];
-  __shared__ float red[kGemvWaves][16][B];
+  __shared__ __attribute__((aligned(16))) uint32_t act_l[kFused ? kGemvWaves : 1][2][64];
+  __shared__ float red[kGemvWaves][kGemvRows][B];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int nv = d_in / kVec;
-  const int row0 = blockIdx.x * 16;
+  const int nrb = (d_out + kBlockRows - 1) / kBlockRows;
+  const int rb0 = blockIdx.x * kGemvTiles;
   const int8_t* act_lo = act + static_cast<size_t>(nb) * d_in;
-  float yp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int base = 0; base < nv; base += kPassChunks) {
-    const int pc = min(kPassChunks, nv - base);           // chunks in this pass
-    const int pieces = pc * (kBytes / 16);                 // 16-byte pieces per row
-    // copy: piece i of row r (rows past d_out are zero)
-    uint4 v[(16 * kPassChunks * kBytes / 16 + 64 * kGemvWaves - 1) / (64 * kGemvWaves)];
+  // uniform base; offsets inside the workgroup's four blocks fit 32 bits (d_in <= 2^24)
+  const uint8_t* wg_rec = packed + static_cast<size_t>(rb0) * nv * kRecord;
+  float yp[kGemvTiles][4];
 #pragma unroll
-    for (int k = 0; k < static_cast<int>(sizeof(v) / sizeof(v[0])); ++k) {
-      const int idx = tid + k * 64 * kGemvWaves;
-      const int r = idx / pieces, pi = idx % pieces;
-      v[k] = make_uint4(0u, 0u, 0u, 0u);
-      if (r < 16 && row0 + r < d_out)
-        v[k] = *reinterpret_cast<const uint4*>(planes + (static_cast<size_t>(row0 + r) * nv + base) * kBytes + pi * 16);
-    }
-    uint16_t sv = 0;
-    const int sr = tid / kPassChunks, sc = tid % kPassChunks;
-    if (tid < 16 * kPassChunks && sc < pc && row0 + sr < d_out) sv = scales[static_cast<size_t>(row0 + sr) * nv + base + sc];
-#pragma unroll
-    for (int k = 0; k < static_cast<int>(sizeof(v) / sizeof(v[0])); ++k) {
-      const int idx = tid + k * 64 * kGemvWaves;
-      const int r = idx / pieces, pi = idx % pieces;
-      if (r < 16) *reinterpret_cast<uint4*>(wl + r * kRowPitch + pi * 16) = v[k];
-    }
-    if (tid < 16 * kPassChunks) sl[tid] = sv;
-    __syncthreads();
+  for (int T = 0; T < kGemvTiles; ++T) yp[T][0] = yp[T][1] = yp[T][2] = yp[T][3] = 0.0f;
 
-    for (int cc = wave; cc < pc; cc += kGemvWaves) {
-      const int c = base + cc;
-      v4i ah[4], al[4];
-      float sg;
-      load_act(act, act_lo, sig, c, nv, nb, r16, g, ah, al, sg);
-      const uint8_t* vp = wl + r16 * kRowPitch + cc * kBytes;
-      const uint4 p1 = *reinterpret_cast<const uint4*>(vp + 16 * g);
-      const uint2 p2 = *reinterpret_cast<const uint2*>(vp + 64 + 8 * g);
-      // 2-bit-plane bytes of octets 4q .. 4q+3 for q = 2g + qq
-      const uint32_t lo0 = __builtin_amdgcn_perm(p1.y, p1.x, 0x06040200u);
-      const uint32_t hi0 = __builtin_amdgcn_perm(p1.y, p1.x, 0x07050301u);
-      const uint32_t lo1 = __builtin_amdgcn_perm(p1.w, p1.z, 0x06040200u);
-      const uint32_t hi1 = __builtin_amdgcn_perm(p1.w, p1.z, 0x07050301u);
-      v4i dh = v4i{0, 0, 0, 0}, dl = v4i{0, 0, 0, 0};
+  for (int c = wave; c < nv; c += kGemvWaves) {
+    // Loads go out in the order they are consumed: the activations first,
+    // then the records, so that each tile's work waits only for its own
+    // record.  None is conditional (a conditional load makes every later
+    // wait a full drain): blocks past the last re-read the last block, whose
+    // outputs are never stored.
+    Act a;
+    uint2 xv;
+    if constexpr (kFused) {
+      xv = *reinterpret_cast<const uint2*>(x + c * kVec + 4 * lane);
+    } else {
+      load_act(act, act_lo, stats, c, nv, nb, r16, g, a);
+    }
+    uint4 p1[kGemvTiles];
+    uint2 p2[kGemvTiles], sc[kGemvTiles];
+#pragma unroll
+    for (int T = 0; T < kGemvTiles; ++T) {
+      const uint32_t o = static_cast<uint32_t>((min(T, nrb - 1 - rb0) * nv + c) * kRecord);
+      p1[T] = *reinterpret_cast<const uint4*>(wg_rec + (o + 16 * lane));
+      p2[T] = *reinterpret_cast<const uint2*>(wg_rec + (o + kHiPlane + 8 * lane));
+      sc[T] = *reinterpret_cast<const uint2*>(wg_rec + (o + kScales + 8 * g));
+    }
+    if constexpr (kFused) {
+      const Split sp = rotate_split(xv, lane);
+      act_l[wave][0][lane] = sp.hi;
+      act_l[wave][1][lane] = sp.lo;
+      wave_lds_sync();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        v4i w;
-        w.x = static_cast<int>(codes4(lo0, hi0, p2.x, 2 * t));
-        w.y = static_cast<int>(codes4(lo0, hi0, p2.x, 2 * t + 1));
-        w.z = static_cast<int>(codes4(lo1, hi1, p2.y, 2 * t));
-        w.w = static_cast<int>(codes4(lo1, hi1, p2.y, 2 * t + 1));
-        dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, ah[t], dh, 0, 0, 0);
-        dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, al[t], dl, 0, 0, 0);
+        a.ah[t] = *reinterpret_cast<const v4i*>(&act_l[wave][0][16 * g + 4 * t]);
+        a.al[t] = *reinterpret_cast<const v4i*>(&act_l[wave][1][16 * g + 4 * t]);
       }
-      // lane holds rows 4g + e of the tile for batch column r16
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        _Float16 hs;
-        const uint16_t sb = sl[(4 * g + e) * kPassChunks + cc];
-        __builtin_memcpy(&hs, &sb, 2);
-        const float s = static_cast<float>(hs) * 0.0625f;
-        yp[e] = fmaf(s * sg, fmaf(static_cast<float>(dl[e]), 0.0078125f, static_cast<float>(dh[e])), yp[e]);
-      }
+      a.sg = sp.sigma;
+      a.sum_hi = sp.sum_hi;
+      a.sum_lo = sp.sum_lo;
     }
-    __syncthreads();
+    const float f = a.sg * (1.0f / 2048.0f);
+#pragma unroll
+    for (int T = 0; T < kGemvTiles; ++T) tile_dot(p1[T], p2[T], sc[T], a, f, yp[T]);
+    if constexpr (kFused) wave_lds_sync();   // this chunk's slot is read before the next chunk rewrites it
   }
   if (r16 < B) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][4 * g + e][r16] = yp[e];
+    for (int T = 0; T < kGemvTiles; ++T) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][16 * T + 4 * g + e][r16] = yp[T][e];
+    }
   }
   __syncthreads();
-  for (int i = tid; i < 16 * B; i += 64 * kGemvWaves) {
+  const int row0 = rb0 * kBlockRows;
+  for (int i = tid; i < kGemvRows * B; i += 64 * kGemvWaves) {
     const int rl = i / B, b = i % B, orow = row0 + rl;
     if (b < nb && orow < d_out) {
       float sum = red[0][rl][b];
@@ -297,27 +409,34 @@ __global__ __launch_bounds__(64 * kGemvWaves) void had256_gemv_i8_kernel(const i
   }
 }
 
-template <int B>
-void launch_gemv(int nb, int d_out, int d_in, const int8_t* act, const float* sig, const uint8_t* planes,
-                 const uint16_t* scales, float* y, hipStream_t s) {
-  hipLaunchKernelGGL(had256_gemv_i8_kernel<B>, dim3((d_out + 15) / 16), dim3(64 * kGemvWaves), 0, s, act, sig, planes,
-                     scales, y, nb, d_out, d_in);
+template <int B, bool kFused>
+void launch_gemv(int nb, int d_out, int d_in, const uint16_t* x, const int8_t* act, const float4* stats,
+                 const uint8_t* packed, float* y, hipStream_t s) {
+  const int nrb = (d_out + kBlockRows - 1) / kBlockRows;
+  hipLaunchKernelGGL((had256_gemv_kernel<B, kFused>), dim3((nrb + kGemvTiles - 1) / kGemvTiles),
+                     dim3(64 * kGemvWaves), 0, s, x, act, stats, packed, y, nb, d_out, d_in);
 }
 
 }  // namespace
 
 extern "C" {
 
-wush_status wush_had256_pack_weights(int d_out, int d_in, const float* W, uint8_t* planes, uint16_t* scales,
-                                     void* stream) {
+size_t wush_had256_packed_bytes(int d_out, int d_in) {
+  if (d_out < 0 || d_in < kVec || d_in % kVec) return 0;
+  return static_cast<size_t>((d_out + kBlockRows - 1) / kBlockRows) * (d_in / kVec) * kRecord;
+}
+
+wush_status wush_had256_pack_weights(int d_out, int d_in, const float* W, uint8_t* packed, void* stream) {
   if (d_out < 0 || d_in < kVec || d_in % kVec)
     return wush::fail(WUSH_E_SHAPE, "wush_had256_pack_weights: d_in must be a positive multiple of 256");
   if (d_out == 0) return WUSH_OK;
-  if (!W || !planes || !scales) return wush::fail(WUSH_E_ARG, "wush_had256_pack_weights: null pointer");
-  const size_t nvec = static_cast<size_t>(d_out) * (d_in / kVec);
+  if (!W || !packed) return wush::fail(WUSH_E_ARG, "wush_had256_pack_weights: null pointer");
+  if (!wush::aligned16(packed)) return wush::fail(WUSH_E_ARG, "wush_had256_pack_weights: packed must be 16-byte aligned");
+  const size_t rows = static_cast<size_t>((d_out + kBlockRows - 1) / kBlockRows) * kBlockRows;
+  const size_t nvec = rows * (d_in / kVec);
   if (nvec > 0x7fffffffu) return wush::fail(WUSH_E_SHAPE, "wush_had256_pack_weights: too many vectors");
   hipLaunchKernelGGL(had256_pack_kernel, dim3(static_cast<unsigned>(nvec)), dim3(kVec), 0,
-                     static_cast<hipStream_t>(stream), W, d_in, planes, scales);
+                     static_cast<hipStream_t>(stream), W, d_out, d_in, packed);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "wush_had256_pack_weights launch: %s", hipGetErrorString(e));
   return WUSH_OK;
@@ -339,18 +458,26 @@ wush_status wush_had256_rotate(int rows, int d_in, const float* in, float* out, 
 
 size_t wush_had256_gemv_ws_bytes(int batch, int d_in) {
   if (batch < 1 || d_in < kVec || d_in % kVec) return 0;
+  if (batch <= kFusedBatch) return 0;                                 // rotated inside the GEMV
   const size_t act = 2 * static_cast<size_t>(batch) * d_in;           // a_hi, a_lo
-  return act + static_cast<size_t>(batch) * (d_in / kVec) * sizeof(float);   // sigma
+  return act + static_cast<size_t>(batch) * (d_in / kVec) * sizeof(float4);   // sigma and sums
 }
 
-wush_status wush_had256_gemv(int batch, int d_out, int d_in, const uint16_t* x, const uint8_t* planes,
-                             const uint16_t* scales, float* y, void* ws, size_t ws_bytes, void* stream) {
-  if (batch < 1 || batch > 16 || d_out < 1 || d_in < kVec || d_in % kVec)
-    return wush::fail(WUSH_E_SHAPE, "wush_had256_gemv: need 1 <= batch <= 16, d_out >= 1, d_in %% 256 == 0");
-  if (!x || !planes || !scales || !y) return wush::fail(WUSH_E_ARG, "wush_had256_gemv: null pointer");
-  if (!wush::aligned16(planes)) return wush::fail(WUSH_E_ARG, "wush_had256_gemv: planes must be 16-byte aligned");
+wush_status wush_had256_gemv(int batch, int d_out, int d_in, const uint16_t* x, const uint8_t* packed, float* y,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 1 || batch > 16 || d_out < 1 || d_in < kVec || d_in % kVec || d_in > (1 << 24))
+    return wush::fail(WUSH_E_SHAPE, "wush_had256_gemv: need 1 <= batch <= 16, d_out >= 1, d_in %% 256 == 0, d_in <= 2^24");
+  if (!x || !packed || !y) return wush::fail(WUSH_E_ARG, "wush_had256_gemv: null pointer");
+  if (!wush::aligned16(packed) || !wush::aligned16(x))
+    return wush::fail(WUSH_E_ARG, "wush_had256_gemv: x and packed must be 16-byte aligned");
   if (ws && !wush::aligned16(ws)) return wush::fail(WUSH_E_ARG, "wush_had256_gemv: workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch <= kFusedBatch) {
+    launch_gemv<kFusedBatch, true>(batch, d_out, d_in, x, nullptr, nullptr, packed, y, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "wush_had256_gemv launch: %s", hipGetErrorString(e));
+    return WUSH_OK;
+  }
   // rotated, int8-split activations: the caller's workspace, else stream-ordered scratch
   const int nv = d_in / kVec;
   const size_t act_bytes = 2 * static_cast<size_t>(batch) * d_in;
@@ -363,14 +490,12 @@ wush_status wush_had256_gemv(int batch, int d_out, int d_in, const uint16_t* x, 
     if (ae != hipSuccess) return wush::fail(WUSH_E_HIP, "wush_had256_gemv scratch (%zu bytes): %s", need, hipGetErrorString(ae));
   }
   int8_t* act = reinterpret_cast<int8_t*>(wsp);
-  float* sig = reinterpret_cast<float*>(wsp + act_bytes);
-  hipLaunchKernelGGL(had256_prep_kernel, dim3(nv, batch), dim3(kVec), 0, s, x, batch, d_in, act, sig);
-  if (batch == 1)
-    launch_gemv<1>(batch, d_out, d_in, act, sig, planes, scales, y, s);
-  else if (batch <= 4)
-    launch_gemv<4>(batch, d_out, d_in, act, sig, planes, scales, y, s);
+  float4* stats = reinterpret_cast<float4*>(wsp + act_bytes);
+  hipLaunchKernelGGL(had256_prep_kernel, dim3(nv, batch), dim3(64), 0, s, x, batch, d_in, act, stats);
+  if (batch <= 4)
+    launch_gemv<4, false>(batch, d_out, d_in, x, act, stats, packed, y, s);
   else
-    launch_gemv<16>(batch, d_out, d_in, act, sig, planes, scales, y, s);
+    launch_gemv<16, false>(batch, d_out, d_in, x, act, stats, packed, y, s);
   const hipError_t fe = ws ? hipSuccess : hipFreeAsync(wsp, s);
   if (fe != hipSuccess) return wush::fail(WUSH_E_HIP, "wush_had256_gemv scratch free: %s", hipGetErrorString(fe));
   hipError_t e = hipGetLastError();

@@ -374,27 +374,28 @@ def bench_had256(args, W, torch):
     Wt = make_weights(wl)
     d_out, d_in = Wt.shape
     dev = "cuda"
-    planes = torch.empty((d_out, d_in // 256, 96), dtype=torch.uint8, device=dev)
-    sc = torch.empty((d_out, d_in // 256), dtype=torch.int16, device=dev)
-    W.wush_had256_pack_weights(torch.from_numpy(Wt).to(dev), planes, sc)
+    packed = torch.empty((W.wush_had256_packed_bytes(d_out, d_in),), dtype=torch.uint8, device=dev)
+    W.wush_had256_pack_weights(torch.from_numpy(Wt).to(dev), packed)
     x = bf16_round(np.random.default_rng([5, 1]).standard_normal((B, d_in)).astype(np.float32))
     xd = torch.from_numpy(bf16_bits(x).view(np.int16)).to(dev)
-    P = [planes] + [planes.clone() for _ in range(args.rotate - 1)]
-    S = [sc] + [sc.clone() for _ in range(args.rotate - 1)]
+    # enough weight copies that they overflow the 256 MB Infinity Cache twice
+    # over, so every step streams its weights from HBM
+    wbytes = packed.numel()
+    nrot = max(args.rotate, -(-2 * 256 * 2**20 // wbytes))
+    P = [packed] + [packed.clone() for _ in range(nrot - 1)]
     y = torch.empty((B, d_out), dtype=torch.float32, device=dev)
     ws = torch.empty(W.wush_had256_gemv_ws_bytes(B, d_in), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        W.wush_had256_gemv(xd, P[i % args.rotate], S[i % args.rotate], y, ws=ws)
+        W.wush_had256_gemv(xd, P[i % nrot], y, ws=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        W.wush_had256_gemv(xd, P[i % args.rotate], S[i % args.rotate], y, ws=ws)
+        W.wush_had256_gemv(xd, P[i % nrot], y, ws=ws)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    wbytes = d_out * (d_in // 256) * 98
     byts = wbytes + B * d_in * 2 + B * d_out * 4
     gbps = byts / (ms / 1e3) / 1e9
     flops = 2.0 * B * d_out * d_in
@@ -402,7 +403,7 @@ def bench_had256(args, W, torch):
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int3+fp32",
            "data": "synthetic",
-           "config": {"workload": wl.name, "batch": B, "d_in": d_in, "d_out": d_out},
+           "config": {"workload": wl.name, "batch": B, "d_in": d_in, "d_out": d_out, "weight_copies": nrot},
            "tflops": round(flops / (ms / 1e3) / 1e12, 3),
            "roofline": {"kernel": "wush_had256_gemv", "bound": "hbm", "achieved": round(gbps, 1),
                         "peak": HBM_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_GBPS, 4), "traffic": None,

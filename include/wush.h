@@ -198,29 +198,43 @@ size_t wush_loss_ws_bytes(int M, int N);
 /* Per 256-vector of every weight row: fp32 FWHT with butterfly stages
  * h = 1, 2, ..., 128, then * 1/16; a = max|v|; s16 = fp16(f32(a/3));
  * q = clamp(rint(f32(v * f32(1/s16))), -3, 3) (all 0 if s16 == 0).
+ * Storage (a layout of this library; the article fixes only 3-bit codes and
+ * an fp16 scale per 256 weights): rows in blocks of 16, the last block
+ * padded with zero rows (q = 0, s16 = 0); one 1568-byte record per (row
+ * block, 256-chunk), records ordered [block][chunk], each holding the codes
+ * c = q + 4 of the block's 16 rows:
+ *   bytes    0..1023: 64 lanes x 16 bytes, lane l = 16 g + r (row r); byte m
+ *                     holds bits 0-1 of codes 64 g + 16 t + m, t = 0..3, at
+ *                     bits 2 t;
+ *   bytes 1024..1535: 64 lanes x 8 bytes; byte 4 j + b holds bit 2 of code
+ *                     64 g + 16 (u / 2) + 8 j + 4 (u % 2) + b at bit u;
+ *   bytes 1536..1567: the 16 rows' fp16 scales.
  *   W       device, [d_out][d_in] fp32, d_in % 256 == 0.
- *   planes  device out, [d_out][d_in/256][96]: bytes 0-63 hold bits 0-1 of
- *           code k (= q & 7) at byte k/4, bit 2*(k%4); bytes 64-95 hold bit 2
- *           of code k at byte 64 + k/8, bit k%8.
- *   scales  device out, [d_out][d_in/256] fp16 bits. */
+ *   packed  device out, wush_had256_packed_bytes(d_out, d_in) bytes,
+ *           16-byte aligned. */
+size_t wush_had256_packed_bytes(int d_out, int d_in);
 wush_status wush_had256_pack_weights(int d_out, int d_in, const float* W,
-                                     uint8_t* planes, uint16_t* scales, void* stream);
+                                     uint8_t* packed, void* stream);
 
 /* y[b][j] = sum_k x[b][k] * w_hat[j][k] with w_hat = s16 * (H_256 q) / 16 per
  * 256-vector (the inverse rotation of the dequantized codes).  Computed as
  * (s16/16) sum_m q_m (H_256 x)_m per vector (H_256 is symmetric), with the
  * rotated activations split into two int8 terms per 256-chunk (relative error
  * below 2^-15 of the chunk's largest value) and exact int32 dot products.
- *   x       device, [batch][d_in] bf16 bits.   y  device out, [batch][d_out] fp32.
+ *   x       device, [batch][d_in] bf16 bits, 16-byte aligned.
+ *   packed  device, the output of wush_had256_pack_weights for (d_out, d_in).
+ *   y       device out, [batch][d_out] fp32.
  *   ws      device scratch of at least wush_had256_gemv_ws_bytes(batch, d_in)
  *           bytes (16-byte aligned), or NULL (taken from the default memory
  *           pool per call, as for wush_w4a4_gemm); calls sharing a ws must be
- *           ordered on one stream.
- * Errors: WUSH_E_SHAPE (batch not in 1..16, d_in % 256), WUSH_E_ARG, WUSH_E_HIP. */
+ *           ordered on one stream.  Batch 1 needs none (size 0): its
+ *           activations are rotated and split inside the GEMV kernel.
+ * Errors: WUSH_E_SHAPE (batch not in 1..16, d_in % 256, d_in > 2^24),
+ * WUSH_E_ARG, WUSH_E_HIP. */
 size_t wush_had256_gemv_ws_bytes(int batch, int d_in);
 wush_status wush_had256_gemv(int batch, int d_out, int d_in, const uint16_t* x,
-                             const uint8_t* planes, const uint16_t* scales,
-                             float* y, void* ws, size_t ws_bytes, void* stream);
+                             const uint8_t* packed, float* y, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Unquantized rotation v = H_256 w / 16 per 256-vector, in place allowed
  * (in == out).  H/16 is orthogonal and its own inverse, so two calls return

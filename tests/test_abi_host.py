@@ -51,16 +51,23 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert L.wush_w4a4_gemm(0, 4, 4, 128, None, None, 1.0, None, None, 1.0, None, None, 0, None) == W.WUSH_E_ARG
     assert L.wush_w4a4_gemm(0, 0, 4, 128, None, None, 1.0, None, None, 1.0, None, None, 0, None) == W.WUSH_E_SHAPE
     assert L.wush_layer_loss(0, 4, None, None, None, None, None) == W.WUSH_E_ARG
-    assert L.wush_had256_gemv(17, 4, 256, None, None, None, None, None, 0, None) == W.WUSH_E_SHAPE
+    assert L.wush_had256_gemv(17, 4, 256, None, None, None, None, 0, None) == W.WUSH_E_SHAPE
+    assert L.wush_had256_gemv(1, 4, (1 << 24) + 256, None, None, None, None, 0, None) == W.WUSH_E_SHAPE
+    assert L.wush_had256_gemv(1, 4, 256, None, None, None, None, 0, None) == W.WUSH_E_ARG
     # workspace sizes (host-side arithmetic only)
-    assert L.wush_had256_gemv_ws_bytes(4, 4096) == 2 * 4 * 4096 + 4 * 16 * 4
+    assert L.wush_had256_gemv_ws_bytes(4, 4096) == 2 * 4 * 4096 + 4 * 16 * 16
+    assert L.wush_had256_packed_bytes(37, 768) == 3 * 3 * 1568       # rows padded to 16-row blocks
+    assert L.wush_had256_packed_bytes(14336, 4096) == 896 * 16 * 1568
+    assert L.wush_had256_packed_bytes(4, 100) == 0
     assert L.wush_had256_gemv_ws_bytes(0, 4096) == 0
+    assert L.wush_had256_gemv_ws_bytes(1, 4096) == 0    # batch 1 rotates inside the GEMV
     assert L.wush_w4a4_gemm_ws_bytes(0, 4096, 12288, 4096) == (16 + 48) * 16 * 2048
     assert L.wush_w4a4_gemm_ws_bytes(0, 4096, 12288, 128) == 0
     assert L.wush_w4a4_gemm_ws_bytes(1, 4096, 12288, 4096) == (16 + 48) * 16 * 8192
     assert L.wush_w4a4_gemm_ws_bytes(1, 4096, 12288, 128) == (16 + 48) * 1 * 8192
     assert L.wush_w4a4_gemm_ws_bytes(2, 4096, 12288, 4096) == 16 * (16 * 8192 + 96 * 4096)
-    assert L.wush_had256_pack_weights(4, 100, None, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_had256_pack_weights(4, 100, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_had256_pack_weights(4, 256, None, None, None) == W.WUSH_E_ARG
     assert L.wush_had256_rotate(4, 256, None, None, None) == W.WUSH_E_ARG
     assert L.wush_loss_ws_bytes(10, 10) >= 8
     # misaligned pointer

@@ -118,21 +118,21 @@ def test_fullsize_had256():
     Wt = make_weights(wl)
     d_out, d_in = Wt.shape
     print(f"[fullsize] {wl.name} d_in={d_in} d_out={d_out}", flush=True)
-    planes = torch.empty((d_out, d_in // 256, 96), dtype=torch.uint8, device=DEV)
-    sc = torch.empty((d_out, d_in // 256), dtype=torch.int16, device=DEV)
-    W.wush_had256_pack_weights(to_dev(Wt), planes, sc)
+    nv, nrb = d_in // 256, d_out // 16
+    packed = torch.empty((W.wush_had256_packed_bytes(d_out, d_in),), dtype=torch.uint8, device=DEV)
+    W.wush_had256_pack_weights(to_dev(Wt), packed)
     torch.cuda.synchronize()
-    rows = _sample(d_out, 64, 5)
-    rp, rs = oh.pack_weights(Wt[rows])
-    assert np.array_equal(host(planes)[rows], rp)
-    assert np.array_equal(host(sc).view(np.uint16)[rows], rs)
+    blocks = _sample(nrb, 6, 5)                       # 16-row blocks, first and last included
+    rows = (16 * blocks[:, None] + np.arange(16)).ravel()
+    rp = oh.pack_weights(Wt[rows])
+    assert np.array_equal(host(packed).reshape(nrb, nv, 1568)[blocks], rp)
     rng = np.random.default_rng([5, 1])
     for B in wl.extra["batches"]:
         x = make_activations(wl, n=B)
         y = torch.full((B, d_out), np.nan, dtype=torch.float32, device=DEV)
-        W.wush_had256_gemv(to_dev(bf16_bits(x).view(np.int16)), planes, sc, y)
+        W.wush_had256_gemv(to_dev(bf16_bits(x).view(np.int16)), packed, y)
         torch.cuda.synchronize()
-        ref = oh.gemv(x, rp, rs)
+        ref = oh.gemv(x, rp, len(rows))
         ok, worst = gemm_close(host(y)[:, rows], ref)
         assert ok, (B, worst)
     # round trip of the unquantized rotation on integer data at full width

@@ -212,14 +212,14 @@ def test_layer_loss():
 
 
 def test_had256_pack_bit_exact_and_rotate():
+    # 37 rows: two full 16-row blocks and one with 11 padding rows
     Wt, _ = random_case(30, 1, 768, 37)
-    planes = torch.empty((37, 3, 96), dtype=torch.uint8, device=DEV)
-    sc = torch.empty((37, 3), dtype=torch.int16, device=DEV)
-    W.wush_had256_pack_weights(to_dev(Wt), planes, sc)
-    rp, rs = oh.pack_weights(Wt)
+    packed = torch.full((W.wush_had256_packed_bytes(37, 768),), 0xA5, dtype=torch.uint8, device=DEV)
+    W.wush_had256_pack_weights(to_dev(Wt), packed)
+    ref = oh.pack_weights(Wt)
     torch.cuda.synchronize()
-    assert np.array_equal(host(sc).view(np.uint16), rs)
-    assert np.array_equal(host(planes), rp)
+    assert packed.numel() == ref.size
+    assert np.array_equal(host(packed).reshape(ref.shape), ref)
     # rotation equals the oracle's butterflies bit for bit; two rotations are exact on integers
     out = torch.empty((37, 768), dtype=torch.float32, device=DEV)
     W.wush_had256_rotate(to_dev(Wt), out)
@@ -233,21 +233,22 @@ def test_had256_pack_bit_exact_and_rotate():
     assert np.array_equal(host(a), ints)
 
 
-# d_in 1280 = 5 chunks (one partial pass of the 16-chunk staging), 5120 = 20
-# chunks (a full pass plus a partial one); d_out 200 leaves a ragged row tile
+# d_in 1280 = 5 chunks (fewer than the 16 waves of a workgroup), 5120 = 20
+# chunks (a second pass for four waves); d_out 200 = 12.5 row blocks: a
+# padded last block and a last workgroup with one of its four blocks
 @pytest.mark.parametrize("batch,d_in", [(1, 1280), (3, 1280), (4, 1280), (5, 1280), (16, 1280), (1, 5120),
                                         (16, 5120)])
 def test_had256_gemv(batch, d_in):
     Wt, _ = random_case(31, 1, d_in, 200)
-    rp, rs = oh.pack_weights(Wt)
+    rp = oh.pack_weights(Wt)
     x = np.random.default_rng(batch).standard_normal((batch, d_in)).astype(np.float32)
     from synth.gen import bf16_round, bf16_bits
     xb = bf16_round(x)
-    ref = oh.gemv(xb, rp, rs)
+    ref = oh.gemv(xb, rp, 200)
     ws = torch.full((W.wush_had256_gemv_ws_bytes(batch, d_in),), 0x5A, dtype=torch.uint8, device=DEV)
     for w in (None, ws):
         y = torch.full((batch, 200), np.nan, dtype=torch.float32, device=DEV)
-        W.wush_had256_gemv(to_dev(bf16_bits(xb).view(np.int16)), to_dev(rp), to_dev(rs.view(np.int16)), y, ws=w)
+        W.wush_had256_gemv(to_dev(bf16_bits(xb).view(np.int16)), to_dev(rp.reshape(-1)), y, ws=w)
         torch.cuda.synchronize()
         ok, worst = gemm_close(host(y), ref)
         assert ok, (w is None, worst)

@@ -100,13 +100,12 @@ def test_fwht_round_trip():
     assert np.all(np.abs(rt - v) <= 16 * 2.0 ** -24 * np.abs(v).max(axis=1, keepdims=True))
 
 
-def test_had256_codes_nearest_and_planes_round_trip():
+def test_had256_codes_nearest_and_record_layout():
     W, _ = random_case(12, 1, 512, 6)
-    planes, scales = had256.pack_weights(W)
-    assert planes.shape == (6, 2, 96) and scales.shape == (6, 2)
-    q = had256.unpack_codes(planes)
+    q, s16 = had256.quantize(W)
+    assert q.shape == (6, 2, 256) and s16.shape == (6, 2)
     v = had256.fwht256(W.reshape(6, 2, 256))
-    s = scales.view(np.float16).astype(np.float32)
+    s = s16.view(np.float16).astype(np.float32)
     r = (np.float32(1) / s).astype(np.float32)
     t = (v * r[..., None]).astype(np.float64)
     lv = np.arange(-3, 4)
@@ -116,26 +115,37 @@ def test_had256_codes_nearest_and_planes_round_trip():
         if len(best) == 2:
             best = best[best % 2 == 0]
         assert qv == best[0]
-    # bit-plane layout: re-pack by explicit bit loops
-    c = (q & 7).astype(int)
-    for o in range(6):
-        for vv in range(2):
+    # record layout, checked bit by bit from its definition; 6 rows -> one
+    # block with 10 padding rows of q = 0 (stored 4) and scale 0
+    rec = had256.pack_weights(W)
+    assert rec.shape == (1, 2, 1568) and had256.packed_bytes(6, 512) == rec.size
+    for vv in range(2):
+        for row in range(16):
             for k in range(256):
-                lo = (planes[o, vv, k // 4] >> (2 * (k % 4))) & 3
-                hi = (planes[o, vv, 64 + k // 8] >> (k % 8)) & 1
-                assert lo | (hi << 2) == c[o, vv, k]
+                c = q[row, vv, k] + 4 if row < 6 else 4
+                g, rest = divmod(k, 64)
+                t, m = divmod(rest, 16)
+                lane = 16 * g + row
+                assert (rec[0, vv, 16 * lane + m] >> (2 * t)) & 3 == c & 3
+                i, b = divmod(m, 4)
+                u = 2 * t + i % 2
+                assert (rec[0, vv, 1024 + 8 * lane + 4 * (i // 2) + b] >> u) & 1 == c >> 2
+            sc = int(rec[0, vv, 1536 + 2 * row]) | (int(rec[0, vv, 1537 + 2 * row]) << 8)
+            assert sc == (int(s16[row, vv]) if row < 6 else 0)
+    q2, s2 = had256.unpack_records(rec, 6)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s16)
 
 
 def test_had256_gemv_matches_decoded_product():
     W, _ = random_case(13, 1, 512, 8)
-    planes, scales = had256.pack_weights(W)
+    rec = had256.pack_weights(W)
     x = np.random.default_rng(14).standard_normal((3, 512))
-    y = had256.gemv(x, planes, scales)
-    w = had256.decode_weights(planes, scales)
+    y = had256.gemv(x, rec, 8)
+    w = had256.decode_weights(rec, 8)
     # decoded weights approximate W (3-bit after rotation)
     assert np.linalg.norm(w - W) / np.linalg.norm(W) < 0.35
     assert np.allclose(y, x @ w.T, rtol=1e-12)
     # the decode is the inverse rotation of s*q: check against the fp32 FWHT on integers
-    q = had256.unpack_codes(planes).astype(np.float32)
-    inv = had256.fwht256(q).astype(np.float64) * scales.view(np.float16).astype(np.float64)[..., None]
+    q, s16 = had256.unpack_records(rec, 8)
+    inv = had256.fwht256(q.astype(np.float32)).astype(np.float64) * s16.view(np.float16).astype(np.float64)[..., None]
     assert np.array_equal(inv.reshape(8, 512), w)
