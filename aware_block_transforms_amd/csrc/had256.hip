@@ -143,6 +143,7 @@ constexpr int kGemvRows = kBlockRows * kGemvTiles;
 constexpr int kFusedBatch = 1;     // batches up to this size rotate their activations inside the GEMV
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Orders this wave's LDS writes before its later LDS reads of other lanes' data.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -151,66 +152,89 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Entry (a, b) of the 16-point Sylvester Hadamard matrix, (-1)^popcount(a & b).
+__device__ __forceinline__ float hsign(int a, int b) { return (__builtin_popcount(a & b) & 1) ? -1.0f : 1.0f; }
+
+// Wave-wide max / sum: DPP butterflies inside each 16-lane row (xor 1, xor 2,
+// then the half-row and row mirrors), then the four row results by readlane.
+template <bool kMax>
+__device__ __forceinline__ uint32_t row_reduce(uint32_t v) {
+  auto op = [](uint32_t x, uint32_t y) { return kMax ? max(x, y) : x + y; };
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row_reduce<true>(v);
+  return max(max(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)),
+                 static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16))),
+             max(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)),
+                 static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48))));
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  const uint32_t r = row_reduce<false>(static_cast<uint32_t>(v));
+  return __builtin_amdgcn_readlane(static_cast<int>(r), 0) + __builtin_amdgcn_readlane(static_cast<int>(r), 16) +
+         __builtin_amdgcn_readlane(static_cast<int>(r), 32) + __builtin_amdgcn_readlane(static_cast<int>(r), 48);
+}
+
 // Rotated, split activations of one chunk of one batch row.
 struct Split {
-  uint32_t hi, lo;    // the lane's 4 int8 terms of elements 4 L .. 4 L + 3
+  uint32_t hi, lo;    // byte e: the int8 terms of element 64 g + 16 e + i of lane (g, i)
   float sigma;
   int sum_hi, sum_lo; // over the whole chunk
 };
 
-// Rotation and int8 split of one 256-chunk on one wave.  Lane L holds
-// elements 4 L + j, j = 0..3 (bf16 in `xv`).  The butterflies are those of
-// fwht256_lds in the same stage order (h = 1, 2 inside the lane, 4 .. 128
-// across lanes L ^ h/4), so the rotated values are bit-identical to it.
+// Rotation and int8 split of one 256-chunk on one wave, on the matrix cores.
+// With the chunk viewed as M[i][k] = x[16 i + k], H_256 x = H_16 M H_16 read
+// row-major (H_256 = H_16 (x) H_16 in Sylvester order).  Lane (g, i) =
+// (lane / 16, lane % 16) passes x[16 i + 4 g .. + 3] (bf16): one bf16 MFMA
+// forms P = M H_16 (exact products, fp32 sums) and four fp32 MFMAs form
+// H_16 P, which leaves element 64 g + 16 e + i in register e of lane (g, i).
 __device__ __forceinline__ Split rotate_split(const uint2& xv, int lane) {
-  float v[4];
-  const uint32_t xw[2] = {xv.x, xv.y};
+  const int g = lane >> 4, i = lane & 15;
+  v4s a, hs;
+  __builtin_memcpy(&a, &xv, 8);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(((xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 16);
+  for (int kk = 0; kk < 4; ++kk) hs[kk] = static_cast<short>(hsign(4 * g + kk, i) < 0.0f ? 0xBF80 : 0x3F80);
+  const v4f p = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hs, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+  v4f r = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int h = 1; h < 4; h <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j & h) continue;
-      const float a = v[j], b = v[j + h];
-      v[j] = a + b;
-      v[j + h] = a - b;
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float o = __shfl_xor(v[j], m);
-      v[j] = upper ? (o - v[j]) : (v[j] + o);
-    }
-  }
+  for (int kk = 0; kk < 4; ++kk) r = __builtin_amdgcn_mfma_f32_16x16x4f32(hsign(i, 4 * g + kk), p[kk], r, 0, 0, 0);
   uint32_t ab = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ab = max(ab, __float_as_uint(v[j]) & 0x7fffffffu);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) ab = max(ab, static_cast<uint32_t>(__shfl_xor(static_cast<int>(ab), m)));
+  for (int e = 0; e < 4; ++e) ab = max(ab, __float_as_uint(r[e]) & 0x7fffffffu);
+  const float amax = __uint_as_float(wave_max_u32(ab));
   Split sp;
-  sp.sigma = __uint_as_float(ab) / 127.0f;
-  sp.hi = sp.lo = 0;
-  int sh = 0, sl = 0;
-  if (sp.sigma > 0.0f) {
+  sp.sigma = amax * (1.0f / 127.0f);
+  // |r| <= amax, so u = r / sigma lies in [-127, 127] up to the reciprocal's
+  // rounding, and (u - hi) * 128 in [-64, 64]: no clamping is needed.  Adding
+  // 1.5 * 2^23 rounds to the nearest integer (ties to even) and leaves it,
+  // two's complement, in the low mantissa byte.
+  const float rs = (amax > 0.0f) ? __builtin_amdgcn_rcpf(sp.sigma) : 0.0f;
+  constexpr float kMagic = 12582912.0f;
+  uint32_t hb[4], lb[4];
+  float shf = 0.0f, slf = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float u = v[j] / sp.sigma;
-      const int hi = static_cast<int>(fminf(fmaxf(rintf(u), -127.0f), 127.0f));
-      const int lo = static_cast<int>(fminf(fmaxf(rintf((u - static_cast<float>(hi)) * 128.0f), -127.0f), 127.0f));
-      sp.hi |= (static_cast<uint32_t>(hi) & 0xFFu) << (8 * j);
-      sp.lo |= (static_cast<uint32_t>(lo) & 0xFFu) << (8 * j);
-      sh += hi;
-      sl += lo;
-    }
+  for (int e = 0; e < 4; ++e) {
+    const float u = r[e] * rs;
+    const float th = u + kMagic;
+    const float hf = th - kMagic;
+    const float tl = (u - hf) * 128.0f + kMagic;
+    hb[e] = __float_as_uint(th);
+    lb[e] = __float_as_uint(tl);
+    shf += hf;
+    slf += tl - kMagic;
   }
+  // low bytes of the four words -> one word (byte e from word e)
+  sp.hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(hb[3], hb[2], 0x0c0c0400u), __builtin_amdgcn_perm(hb[1], hb[0], 0x0c0c0400u), 0x05040100u);
+  sp.lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(lb[3], lb[2], 0x0c0c0400u), __builtin_amdgcn_perm(lb[1], lb[0], 0x0c0c0400u), 0x05040100u);
   // both sums are within +-256 * 127, so one int32 carries them: 65536 sh + sl
-  int packed = sh * 65536 + sl;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) packed += __shfl_xor(packed, m);
+  const int packed = wave_sum_i32(static_cast<int>(shf) * 65536 + static_cast<int>(slf));
   sp.sum_lo = static_cast<int>(static_cast<int16_t>(packed & 0xFFFF));
   sp.sum_hi = (packed - sp.sum_lo) / 65536;
   return sp;
@@ -225,12 +249,18 @@ __global__ __launch_bounds__(64) void had256_prep_kernel(const uint16_t* __restr
                                                          int8_t* __restrict__ act, float4* __restrict__ stats) {
   const int lane = threadIdx.x, c = blockIdx.x, b = blockIdx.y;
   const int nv = d_in / kVec;
-  const uint2 xv = *reinterpret_cast<const uint2*>(x + static_cast<size_t>(b) * d_in + c * kVec + 4 * lane);
+  const int g = lane >> 4, i = lane & 15;
+  const uint2 xv =
+      *reinterpret_cast<const uint2*>(x + static_cast<size_t>(b) * d_in + c * kVec + 16 * i + 4 * g);
   const Split sp = rotate_split(xv, lane);
-  // lane L holds elements 4 L .. 4 L + 3: g = L / 16, t = (L / 4) % 4, p = 4 (L % 4)
-  const size_t o = ((static_cast<size_t>(c) * 16 + ((lane >> 2) & 3) * 4 + (lane >> 4)) * batch + b) * 16 + 4 * (lane & 3);
-  *reinterpret_cast<uint32_t*>(act + o) = sp.hi;
-  *reinterpret_cast<uint32_t*>(act + static_cast<size_t>(batch) * d_in + o) = sp.lo;
+  // element 64 g + 16 e + i is byte i of operand (t = e, g)
+  const size_t lo_off = static_cast<size_t>(batch) * d_in;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const size_t o = ((static_cast<size_t>(c) * 16 + 4 * e + g) * batch + b) * 16 + i;
+    act[o] = static_cast<int8_t>(sp.hi >> (8 * e));
+    act[lo_off + o] = static_cast<int8_t>(sp.lo >> (8 * e));
+  }
   if (lane == 0)
     stats[static_cast<size_t>(b) * nv + c] =
         make_float4(sp.sigma, __int_as_float(sp.sum_hi), __int_as_float(sp.sum_lo), 0.0f);
@@ -315,7 +345,7 @@ __device__ __forceinline__ void tile_dot(const uint4& p1, const uint2& p2, const
     const uint16_t sb = static_cast<uint16_t>(sw[e >> 1] >> (16 * (e & 1)));
     __builtin_memcpy(&hs, &sb, 2);
     const int d = dh[e] * 128 + dl[e];
-    yp[e] = fmaf(static_cast<float>(hs) * f, static_cast<float>(d), yp[e]);
+    yp[e] = fmaf(static_cast<float>(hs), f * static_cast<float>(d), yp[e]);
   }
 }
 
@@ -334,16 +364,19 @@ __global__ __launch_bounds__(64 * kGemvWaves) void had256_gemv_kernel(
     const uint8_t* __restrict__ packed, float* __restrict__ y, int nb, int d_out, int d_in) {
   static_assert(!kFused || B == 1, "the in-kernel rotation serves one batch row");
   // B is the compiled batch capacity; nb <= B rows of x / y are real.
-  __shared__ __attribute__((aligned(16))) uint32_t act_l[kFused ? kGemvWaves : 1][2][64];
+  __shared__ __attribute__((aligned(16))) int8_t act_l[kFused ? kGemvWaves : 1][2][4][4][16];   // [.][hi/lo][g][t][p]
   __shared__ float red[kGemvWaves][kGemvRows][B];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: chunk addresses stay scalar
   const int r16 = lane & 15, g = lane >> 4;
   const int nv = d_in / kVec;
   const int nrb = (d_out + kBlockRows - 1) / kBlockRows;
   const int rb0 = blockIdx.x * kGemvTiles;
   const int8_t* act_lo = act + static_cast<size_t>(nb) * d_in;
-  // uniform base; offsets inside the workgroup's four blocks fit 32 bits (d_in <= 2^24)
+  // the workgroup's records as one buffer: offsets fit 32 bits (d_in <= 2^24)
   const uint8_t* wg_rec = packed + static_cast<size_t>(rb0) * nv * kRecord;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wg_rec), 0, min(kGemvTiles, nrb - rb0) * nv * kRecord, 0x00020000);
   float yp[kGemvTiles][4];
 #pragma unroll
   for (int T = 0; T < kGemvTiles; ++T) yp[T][0] = yp[T][1] = yp[T][2] = yp[T][3] = 0.0f;
@@ -357,28 +390,39 @@ __global__ __launch_bounds__(64 * kGemvWaves) void had256_gemv_kernel(
     Act a;
     uint2 xv;
     if constexpr (kFused) {
-      xv = *reinterpret_cast<const uint2*>(x + c * kVec + 4 * lane);
+      xv = *reinterpret_cast<const uint2*>(x + c * kVec + 16 * r16 + 4 * g);
     } else {
       load_act(act, act_lo, stats, c, nv, nb, r16, g, a);
     }
     uint4 p1[kGemvTiles];
     uint2 p2[kGemvTiles], sc[kGemvTiles];
+    // buffer loads: the record's offset is uniform (scalar), the three lane
+    // offsets are the same for every record
 #pragma unroll
     for (int T = 0; T < kGemvTiles; ++T) {
-      const uint32_t o = static_cast<uint32_t>((min(T, nrb - 1 - rb0) * nv + c) * kRecord);
-      p1[T] = *reinterpret_cast<const uint4*>(wg_rec + (o + 16 * lane));
-      p2[T] = *reinterpret_cast<const uint2*>(wg_rec + (o + kHiPlane + 8 * lane));
-      sc[T] = *reinterpret_cast<const uint2*>(wg_rec + (o + kScales + 8 * g));
+      const int so = (min(T, nrb - 1 - rb0) * nv + c) * kRecord;
+      const v4i v1 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * lane, so, 0);
+      const v2i v2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, kHiPlane + 8 * lane, so, 0);
+      const v2i v3 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, kScales + 8 * g, so, 0);
+      p1[T] = make_uint4(v1.x, v1.y, v1.z, v1.w);
+      p2[T] = make_uint2(v2.x, v2.y);
+      sc[T] = make_uint2(v3.x, v3.y);
     }
+    // keep every load above issued before any work that waits on one of them
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (kFused) {
       const Split sp = rotate_split(xv, lane);
-      act_l[wave][0][lane] = sp.hi;
-      act_l[wave][1][lane] = sp.lo;
+      // element 64 g + 16 e + r16 is byte r16 of operand (t = e, g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        act_l[wave][0][g][e][r16] = static_cast<int8_t>(sp.hi >> (8 * e));
+        act_l[wave][1][g][e][r16] = static_cast<int8_t>(sp.lo >> (8 * e));
+      }
       wave_lds_sync();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        a.ah[t] = *reinterpret_cast<const v4i*>(&act_l[wave][0][16 * g + 4 * t]);
-        a.al[t] = *reinterpret_cast<const v4i*>(&act_l[wave][1][16 * g + 4 * t]);
+        a.ah[t] = *reinterpret_cast<const v4i*>(&act_l[wave][0][g][t][0]);
+        a.al[t] = *reinterpret_cast<const v4i*>(&act_l[wave][1][g][t][0]);
       }
       a.sg = sp.sigma;
       a.sum_hi = sp.sum_hi;
