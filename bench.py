@@ -406,7 +406,8 @@ def bench_had256(args, W, torch):
            "config": {"workload": wl.name, "batch": B, "d_in": d_in, "d_out": d_out, "weight_copies": nrot},
            "tflops": round(flops / (ms / 1e3) / 1e12, 3),
            "roofline": {"kernel": "wush_had256_gemv", "bound": "hbm", "achieved": round(gbps, 1),
-                        "peak": HBM_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_GBPS, 4), "traffic": None,
+                        "peak": HBM_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_GBPS, 4),
+                        "traffic": measured_traffic("wush_had256_gemv_b%d" % B, wl.name),
                         "avg_us": round(ms * 1e3, 2)}}
     print(json.dumps(out), flush=True)
 
