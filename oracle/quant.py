@@ -130,6 +130,46 @@ def quant_int4(y):
     return pack_nibbles(codes.reshape(y.shape)), scale
 
 
+def apply_hd(d, Xt, bs):
+    """Hadamard-diagonal transform y = H_bs (d o x) per block and token, fp32.
+
+    Pinned: v_k = f32(x_k * d_k) (a product, not fused into the butterflies),
+    then butterfly stages h = 1, 2, ..., bs/2; in each stage every pair
+    (j, j + h) with j in the lower half of a 2h-aligned group becomes
+    (v_j + v_{j+h}, v_j - v_{j+h}), in fp32.
+    d: [d_in] float32 (the Hadamard's 1/sqrt(bs) included); Xt: [n][d_in].
+    """
+    Xt = np.asarray(Xt, dtype=np.float32)
+    n, d_in = Xt.shape
+    v = (Xt * np.asarray(d, dtype=np.float32)[None, :]).astype(np.float32)
+    h = 1
+    while h < bs:
+        w = v.reshape(n, d_in // (2 * h), 2, h)
+        lo = w[:, :, 0, :].copy()
+        hi = w[:, :, 1, :].copy()
+        w[:, :, 0, :] = lo + hi
+        w[:, :, 1, :] = lo - hi
+        v = w.reshape(n, d_in)
+        h *= 2
+    return v
+
+
+def quantize(fmt, y, g=None):
+    """Block quantizer of an already transformed [n][d_in] fp32 array."""
+    if fmt == "mxfp4":
+        return quant_mxfp4(y)
+    if fmt == "nvfp4":
+        return quant_nvfp4(y, g)
+    if fmt == "int4":
+        return quant_int4(y)
+    raise ValueError(fmt)
+
+
+def transform_quant_hd(fmt, d, Xt, g=None):
+    """Hadamard-diagonal activation step: apply_hd then the block quantizer."""
+    return quantize(fmt, apply_hd(d, Xt, BLOCK[fmt]), g)
+
+
 def transform_quant(fmt, T, Xt, g=None, identity=False):
     """Full activation-side step: transform then quantize.  Returns (codes, scales)."""
     y = apply_transform(T, Xt, identity=identity)

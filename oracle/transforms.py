@@ -32,7 +32,7 @@ on FP optimality states), whose minimum is (sum sigma_i)^2.
 
 import numpy as np
 
-KINDS = ("identity", "hadamard", "wus", "wush")
+KINDS = ("identity", "hadamard", "wus", "wush")     # the dense kinds; build_hd is the diagonal variant
 DAMPING = (0.0, 1e-10, 1e-8, 1e-6, 1e-4, 1e-2)
 SIGMA_FLOOR = 1e-12
 
@@ -150,6 +150,57 @@ def build_transforms(kind, Wt, Sx, bs):
         Bb = np.asarray(Sx[b], dtype=np.float64) if Sx is not None else None
         Tx64[b], Tw64[b] = block_transform(kind, Ab, Bb, bs)
     return Tx64.astype(np.float32), Tw64.astype(np.float32), Tx64, Tw64
+
+
+# ---------------------------------------------------------------------------
+# Hadamard-diagonal variant.  The news article's paragraphs on deployment and
+# on limitations propose approximating the data-aware component by a diagonal
+# matrix.  Reading used here: keep the orthonormal Hadamard and replace
+# S^{-1/2} U^T W'^T by what the same construction gives for diagonal moments
+# a_i = (W_b W_b^T)_ii and b_i = (B_b)_ii (W' = diag(sqrt a), U = I,
+# lam = a b):
+#     T_X = H^ diag((a_i / b_i)^{1/4}),   T_W = H^ diag((b_i / a_i)^{1/4}) = T_X^{-T}.
+# Among T_W = H^ E with E diagonal it minimises the proxy J, because
+# J = (sum e_i^2 a_i)(sum b_i / e_i^2) >= (sum sqrt(a_i b_i))^2 (Cauchy-Schwarz)
+# with equality at e_i^4 proportional to b_i / a_i.  Moments below 1e-12 of
+# the block's largest are floored; an all-zero activation block uses b = 1 (as
+# the full builder's sigma fallback does) and an all-zero weight block is an
+# error (as the full builder's Cholesky is).  The scales carry the Hadamard's
+# 1/sqrt(bs): d = sqrt(sqrt(ratio)) / sqrt(bs), so that T = H diag(d) with H
+# the +-1 Sylvester matrix.
+
+HD_FLOOR = 1e-12
+
+
+def hd_block_scales(a, b, bs):
+    """(d_x, d_w) of one block from the moment diagonals a, b (fp64, length bs)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if not a.max() > 0:
+        raise np.linalg.LinAlgError("block weights are all zero")
+    a = np.maximum(a, HD_FLOOR * a.max())
+    b = np.maximum(b, HD_FLOOR * b.max()) if b.max() > 0 else np.ones_like(b)
+    inv = 1.0 / np.sqrt(bs)
+    return np.sqrt(np.sqrt(a / b)) * inv, np.sqrt(np.sqrt(b / a)) * inv
+
+
+def build_hd(Wt, Sx, bs):
+    """Per-channel scales (dx, dw): float32 [d_in] each, plus their fp64 values."""
+    A = weight_moments(Wt, bs)
+    a = np.diagonal(A, axis1=1, axis2=2)
+    b = np.diagonal(np.asarray(Sx, dtype=np.float64), axis1=1, axis2=2)
+    dx = np.empty(a.shape)
+    dw = np.empty(a.shape)
+    for k in range(a.shape[0]):
+        dx[k], dw[k] = hd_block_scales(a[k], b[k], bs)
+    dx, dw = dx.reshape(-1), dw.reshape(-1)
+    return dx.astype(np.float32), dw.astype(np.float32), dx, dw
+
+
+def hd_dense(d, bs):
+    """The block matrices H diag(d_b) that per-channel scales d [d_in] stand for (fp64)."""
+    d = np.asarray(d, dtype=np.float64).reshape(-1, bs)
+    return hadamard(bs)[None, :, :] * d[:, None, :]
 
 
 def proxy_loss(T, A, B):

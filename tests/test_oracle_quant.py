@@ -164,3 +164,44 @@ def test_tiny_workload_loss_ordering():
         loss[kind] = gemm.layer_loss(Y, Yref)
     assert loss["wush"] <= loss["hadamard"] <= loss["identity"], loss
     assert loss["wush"] < 0.5 * loss["identity"], loss
+
+
+# ---------------------------------------------------------------------------
+# Hadamard-diagonal transform (pinned fp32 butterflies)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_apply_hd_matches_dense_product(bs):
+    from oracle import transforms as tr
+    rng = np.random.default_rng(40 + bs)
+    x = rng.standard_normal((50, 4 * bs)).astype(np.float32)
+    d = rng.uniform(0.05, 0.4, 4 * bs).astype(np.float32)
+    y = quant.apply_hd(d, x, bs).astype(np.float64)
+    T = tr.hd_dense(d, bs)                                    # H diag(d) per block
+    ref = np.einsum("bij,nbj->nbi", T, x.astype(np.float64).reshape(50, 4, bs)).reshape(50, 4 * bs)
+    # log2(bs) rounded stages after one rounded product
+    tol = (np.log2(bs) + 1) * 2.0 ** -24 * np.abs(x * d).reshape(50, 4, bs).sum(-1, keepdims=True)
+    assert np.all(np.abs(y - ref).reshape(50, 4, bs) <= tol)
+
+
+def test_apply_hd_is_exact_on_integers_and_signs_follow_sylvester():
+    import scipy.linalg
+    rng = np.random.default_rng(44)
+    x = rng.integers(-1000, 1001, (20, 64)).astype(np.float32)
+    y = quant.apply_hd(np.ones(64, np.float32), x, 32)
+    H = scipy.linalg.hadamard(32)
+    ref = np.einsum("ij,nbj->nbi", H, x.astype(np.int64).reshape(20, 2, 32)).reshape(20, 64)
+    assert np.array_equal(y.astype(np.int64), ref)
+    # one-hot inputs read out the matrix columns, signs included
+    e = np.zeros((32, 32), np.float32)
+    np.fill_diagonal(e, 1.0)
+    assert np.array_equal(quant.apply_hd(np.ones(32, np.float32), e, 32), H.T.astype(np.float32))
+
+
+def test_transform_quant_hd_is_apply_then_quantize():
+    rng = np.random.default_rng(45)
+    x = rng.standard_normal((16, 128)).astype(np.float32)
+    d = rng.uniform(0.1, 0.3, 128).astype(np.float32)
+    c1, s1 = quant.transform_quant_hd("mxfp4", d, x)
+    c2, s2 = quant.quant_mxfp4(quant.apply_hd(d, x, 32))
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)

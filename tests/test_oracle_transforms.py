@@ -165,3 +165,82 @@ def test_tiny_workload_builds():
     for kind in ("identity", "hadamard", "wush"):
         Tx, Tw, _, _ = tr.build_transforms(kind, W, B, 32)
         assert Tx.shape == (8, 32, 32) and np.all(np.isfinite(Tx)) and np.all(np.isfinite(Tw))
+
+
+# ---------------------------------------------------------------------------
+# Hadamard-diagonal variant (the pages' diagonal approximation of the
+# data-aware component; reading in the oracle's transforms module)
+
+
+def test_hd_scales_are_the_optimal_diagonal_and_inverse_transpose():
+    W, X, A, B = _case(seed=31)
+    dx, dw, dx64, dw64 = tr.build_hd(W, B.astype(np.float32), 32)
+    Tx = tr.hd_dense(dx64, 32)
+    Tw = tr.hd_dense(dw64, 32)
+    for b in range(A.shape[0]):
+        a, bb = np.diag(A[b]), np.diag(B[b].astype(np.float32).astype(np.float64))
+        # T_W^T T_X = I
+        assert np.allclose(Tw[b].T @ Tx[b], np.eye(32), atol=1e-12)
+        # the proxy reaches the Cauchy-Schwarz bound (sum sqrt(a b))^2 ...
+        J = tr.proxy_loss(Tw[b], A[b], B[b].astype(np.float32).astype(np.float64))
+        J_diag_bound = np.sum(np.sqrt(a * bb)) ** 2
+        # ... which only holds for the diagonal of the moments; with the full
+        # moments J is tr(E A E) tr(E^-1 B E^-1) evaluated on the off-diagonals too
+        E = np.diag(dw64.reshape(-1, 32)[b] * np.sqrt(32))
+        Ei = np.linalg.inv(E)
+        assert np.isclose(J, np.trace(E @ A[b] @ E) * np.trace(Ei @ B[b].astype(np.float32).astype(np.float64) @ Ei),
+                          rtol=1e-10)
+        assert np.isclose(np.sum(np.diag(E) ** 2 * a) * np.sum(bb / np.diag(E) ** 2), J_diag_bound, rtol=1e-10)
+        # no other diagonal does better on the diagonal model
+        rng = np.random.default_rng(b)
+        for _ in range(20):
+            e = np.diag(E) * np.exp(0.3 * rng.standard_normal(32))
+            assert np.sum(e ** 2 * a) * np.sum(bb / e ** 2) >= J_diag_bound * (1 - 1e-12)
+
+
+def test_hd_sits_between_wush_and_hadamard():
+    W, X, A, B = _case(seed=32)
+    B32 = B.astype(np.float32)
+    _, _, dx64, dw64 = tr.build_hd(W, B32, 32)
+    Tw_hd = tr.hd_dense(dw64, 32)
+    for b in range(A.shape[0]):
+        Bb = B32[b].astype(np.float64)
+        _, Tw_w = tr.block_transform("wush", A[b], Bb, 32)
+        _, Tw_h = tr.block_transform("hadamard", A[b], Bb, 32)
+        j_w = tr.proxy_loss(Tw_w, A[b], Bb)
+        j_h = tr.proxy_loss(Tw_h, A[b], Bb)
+        # the diagonal model's optimum, evaluated on the diagonal moments
+        a, bb = np.diag(A[b]), np.diag(Bb)
+        assert j_w <= tr.proxy_loss(Tw_hd[b], A[b], Bb) * (1 + 1e-9)
+        assert np.sum(np.sqrt(a * bb)) ** 2 <= np.sum(a) * np.sum(bb) * (1 + 1e-12)
+        assert j_h == pytest.approx(np.trace(A[b]) * np.trace(Bb), rel=1e-9)
+
+
+def test_hd_equals_wush_on_diagonal_moments():
+    # with diagonal moments the full construction has nothing off the diagonal
+    # to exploit: both reach (sum sqrt(a b))^2
+    rng = np.random.default_rng(33)
+    a = rng.uniform(0.1, 10, 32)
+    bb = rng.uniform(0.1, 10, 32)
+    A, B = np.diag(a), np.diag(bb)
+    _, Tw_w = tr.block_transform("wush", A, B, 32)
+    dx, dw = tr.hd_block_scales(a, bb, 32)
+    Tw = tr.hd_dense(dw, 32)[0]
+    bound = np.sum(np.sqrt(a * bb)) ** 2
+    assert tr.proxy_loss(Tw, A, B) == pytest.approx(bound, rel=1e-12)
+    assert tr.proxy_loss(Tw_w, A, B) == pytest.approx(bound, rel=1e-9)
+    # the scales themselves: closed form (a / b)^(1/4) / sqrt(32)
+    assert np.allclose(dx, (a / bb) ** 0.25 / np.sqrt(32), rtol=1e-15)
+    assert np.allclose(dx * dw, np.full(32, 1.0 / 32), rtol=1e-15)
+
+
+def test_hd_floors_and_zero_blocks():
+    a = np.array([4.0, 0.0] + [1.0] * 30)
+    bb = np.array([0.0, 2.0] + [1.0] * 30)
+    dx, dw = tr.hd_block_scales(a, bb, 32)
+    assert np.all(np.isfinite(dx)) and np.all(np.isfinite(dw)) and np.all(dx > 0)
+    assert dx[0] == pytest.approx((4.0 / (1e-12 * 2.0)) ** 0.25 / np.sqrt(32))
+    dx0, dw0 = tr.hd_block_scales(a, np.zeros(32), 32)       # all-zero activations: b = 1
+    assert np.allclose(dx0, np.sqrt(np.sqrt(np.maximum(a, 4e-12))) / np.sqrt(32))
+    with pytest.raises(np.linalg.LinAlgError):
+        tr.hd_block_scales(np.zeros(32), bb, 32)
