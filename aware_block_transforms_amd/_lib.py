@@ -44,6 +44,10 @@ _SIGS = {
     "wush_transform_quant": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _p], _i),
     "wush_nvfp4_global_scale": ([_i, _i, _i, _p, _p, _fp, _p], _i),
     "wush_pack_weights": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
+    "wush_build_hd": ([_i, _i, _i, _p, _p, _p, _p], _i),
+    "wush_transform_quant_hd": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _p], _i),
+    "wush_nvfp4_global_scale_hd": ([_i, _i, _i, _p, _p, _fp, _p], _i),
+    "wush_pack_weights_hd": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
     "wush_w4a4_gemm_ws_bytes": ([_i, _i, _i, _i], _sz),
     "wush_w4a4_gemm": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _f, _p, _p, _sz, _p], _i),
     "wush_layer_loss": ([_i, _i, _p, _p, _p, _p, _p], _i),
@@ -114,6 +118,12 @@ def wush_build_transforms(kind, bs, W, Sx, Tx, Tw):
            "wush_build_transforms")
 
 
+def wush_build_hd(bs, W, Sx, dx, dw):
+    """Host arrays: W [d_out][d_in] f32, Sx [nblk][bs][bs] f32; dx, dw out [d_in] f32."""
+    d_out, d_in = W.shape
+    _check(lib.wush_build_hd(bs, d_in, d_out, _ptr(W), _ptr(Sx), _ptr(dx), _ptr(dw)), "wush_build_hd")
+
+
 # ----------------------------------------------------------------------------- device calls
 
 
@@ -144,6 +154,36 @@ def wush_pack_weights(fmt, W, Tw, codes, scales, stream=None):
     g = ctypes.c_float(0.0)
     _check(lib.wush_pack_weights(_fmt(fmt), d_out, d_in, _ptr(W), _ptr(Tw), _ptr(codes), _ptr(scales),
                                  ctypes.byref(g), _stream(stream)), "wush_pack_weights")
+    return g.value
+
+
+def wush_transform_quant_hd(fmt, X, dx, codes, scales, g=0.0, stream=None):
+    """Hadamard-diagonal variant; dx: device [d_in] f32 (from wush_build_hd)."""
+    import torch
+    n, d_in = X.shape
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("X must be float32 or bfloat16")
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    _check(lib.wush_transform_quant_hd(_fmt(fmt), xdt, n, d_in, _ptr(X), _ptr(dx), float(g), _ptr(codes),
+                                       _ptr(scales), _stream(stream)), "wush_transform_quant_hd")
+
+
+def wush_nvfp4_global_scale_hd(X, dx, stream=None):
+    import torch
+    n, d_in = X.shape
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    g = ctypes.c_float(0.0)
+    _check(lib.wush_nvfp4_global_scale_hd(xdt, n, d_in, _ptr(X), _ptr(dx), ctypes.byref(g), _stream(stream)),
+           "wush_nvfp4_global_scale_hd")
+    return g.value
+
+
+def wush_pack_weights_hd(fmt, W, dw, codes, scales, stream=None):
+    """W: device [d_out][d_in] f32, dw: device [d_in] f32.  Returns the NVFP4 tensor scale (1.0 otherwise)."""
+    d_out, d_in = W.shape
+    g = ctypes.c_float(0.0)
+    _check(lib.wush_pack_weights_hd(_fmt(fmt), d_out, d_in, _ptr(W), _ptr(dw), _ptr(codes), _ptr(scales),
+                                    ctypes.byref(g), _stream(stream)), "wush_pack_weights_hd")
     return g.value
 
 

@@ -225,6 +225,10 @@ bool block_transform(bool with_h, int bs, const double* A, const double* B, doub
 
 using wush::fail;
 
+namespace {
+constexpr double kHdFloor = 1e-12;   // moments below this fraction of the block's largest are floored
+}
+
 extern "C" {
 
 const char* wush_status_string(wush_status s) {
@@ -326,6 +330,47 @@ wush_status wush_build_transforms(wush_kind kind, int bs, int d_in, int d_out, c
   if (bad_block.load() >= 0)
     return fail(WUSH_E_NUMERIC, "wush_build_transforms: block %d weight moment not positive definite after damping",
                 bad_block.load());
+  return WUSH_OK;
+}
+
+// Hadamard-diagonal variant (news article, deployment and limitation
+// paragraphs: the data-aware component approximated by a diagonal matrix).
+// From the moment diagonals a_i = sum_o W[o][i]^2 and b_i = Sx_b[i][i]:
+// d_x = sqrt(sqrt(a / b)) / sqrt(bs), d_w = sqrt(sqrt(b / a)) / sqrt(bs),
+// the optimum of the proxy among Hadamard-times-diagonal transforms.
+wush_status wush_build_hd(int bs, int d_in, int d_out, const float* W, const float* Sx, float* dx, float* dw) {
+  WUSH_REQUIRE(W && Sx && dx && dw, WUSH_E_ARG, "wush_build_hd: null pointer");
+  WUSH_REQUIRE(bs == 16 || bs == 32, WUSH_E_SHAPE, "wush_build_hd: bs must be 16 or 32 (got %d)", bs);
+  WUSH_REQUIRE(d_in >= bs && d_in % bs == 0, WUSH_E_SHAPE, "wush_build_hd: d_in %% bs != 0 (d_in=%d)", d_in);
+  WUSH_REQUIRE(d_out >= 1, WUSH_E_SHAPE, "wush_build_hd: d_out must be >= 1");
+  const int nblk = d_in / bs;
+  const double inv = 1.0 / std::sqrt(static_cast<double>(bs));
+  std::atomic<int> bad_block{-1};
+  wush::parallel_blocks(nblk, [&](int b) {
+    std::vector<double> a(bs, 0.0), s(bs);
+    for (int o = 0; o < d_out; ++o) {
+      const float* w = W + static_cast<size_t>(o) * d_in + static_cast<size_t>(b) * bs;
+      for (int i = 0; i < bs; ++i) a[i] += static_cast<double>(w[i]) * static_cast<double>(w[i]);
+    }
+    double amax = 0.0, smax = 0.0;
+    for (int i = 0; i < bs; ++i) {
+      s[i] = Sx[(static_cast<size_t>(b) * bs + i) * bs + i];
+      amax = std::max(amax, a[i]);
+      smax = std::max(smax, s[i]);
+    }
+    if (!(amax > 0.0)) {
+      bad_block = b;
+      return;
+    }
+    for (int i = 0; i < bs; ++i) {
+      const double ai = std::max(a[i], kHdFloor * amax);
+      const double si = smax > 0.0 ? std::max(s[i], kHdFloor * smax) : 1.0;
+      dx[b * bs + i] = static_cast<float>(std::sqrt(std::sqrt(ai / si)) * inv);
+      dw[b * bs + i] = static_cast<float>(std::sqrt(std::sqrt(si / ai)) * inv);
+    }
+  });
+  if (bad_block.load() >= 0)
+    return fail(WUSH_E_NUMERIC, "wush_build_hd: block %d has all-zero weights", bad_block.load());
   return WUSH_OK;
 }
 

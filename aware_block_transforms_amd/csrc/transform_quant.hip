@@ -265,6 +265,76 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves
   }
 }
 
+// Hadamard-diagonal variant (news article, deployment and limitation
+// paragraphs: the data-aware component approximated by a diagonal matrix):
+// y = H_bs (d o x) per block, pinned as one fp32 product per element and then
+// butterfly stages h = 1, 2, ..., bs/2 (no fused multiply-add).  With bs + 5
+// operations per element instead of 2 bs, the step is bound by HBM, so the
+// mapping is chosen for the memory stream: one lane per (token, block), the
+// lanes of a wave on 64 consecutive blocks of one token row (contiguous 64 B
+// per lane, 4 KB per wave at bs 32 and bf16), each wave on kHdTokens tokens,
+// whose loads are all issued before the first is used.  The lane's d values
+// stay in VGPRs.
+constexpr int kHdTokens = 2;
+
+template <int BS>
+__device__ __forceinline__ void hd_rotate(float (&v)[BS]) {
+#pragma unroll
+  for (int h = 1; h < BS; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+      if (j & h) continue;
+      const float a = v[j], b = v[j + h];
+      v[j] = a + b;
+      v[j + h] = a - b;
+    }
+  }
+}
+
+template <int BS, int FMT, bool BF16>
+__global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_hd_kernel(
+    const void* __restrict__ X, const float* __restrict__ d, int n, int d_in, float g,
+    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nblk = d_in / BS;
+  const int blk = blockIdx.x * kWave + lane;
+  const bool vb = blk < nblk;
+  const int tok0 = (blockIdx.y * kWavesPerGroup + wave) * kHdTokens;
+  // Loads are unconditional (a conditional load makes every later wait a full
+  // drain): lanes past the last block and tokens past n re-read the last one,
+  // and only the stores below are guarded.
+  const size_t col = static_cast<size_t>(min(blk, nblk - 1)) * BS;
+  uint32_t run_max = 0;
+  float x[kHdTokens][BS];
+#pragma unroll
+  for (int t = 0; t < kHdTokens; ++t)
+    load_block<BS, BF16>(X, static_cast<size_t>(min(tok0 + t, n - 1)) * d_in + col, x[t]);
+  float dv[BS];
+  {
+    const float4* p = reinterpret_cast<const float4*>(d + col);
+#pragma unroll
+    for (int q = 0; q < BS / 4; ++q) {
+      const float4 w = p[q];
+      dv[4 * q + 0] = w.x; dv[4 * q + 1] = w.y; dv[4 * q + 2] = w.z; dv[4 * q + 3] = w.w;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kHdTokens; ++t) {
+    if (vb && tok0 + t < n) {
+#pragma unroll
+      for (int k = 0; k < BS; ++k) x[t][k] = x[t][k] * dv[k];
+      hd_rotate<BS>(x[t]);
+      encode_store<BS, FMT>(x[t], static_cast<size_t>(tok0 + t), blk, nblk, d_in, g, codes, scales, run_max);
+    }
+  }
+  if constexpr (FMT == kAmax) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) run_max = max(run_max, static_cast<uint32_t>(__shfl_xor(static_cast<int>(run_max), off)));
+    if (lane == 0) atomicMax(amax_out, run_max);
+  }
+}
+
 __global__ void fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
 using KernelFn = void (*)(const void*, const float*, int, int, float, uint8_t*, void*, uint32_t*);
@@ -305,18 +375,51 @@ wush_status launch(int fmt, int bs, bool bf16, int n, int d_in, const void* X, c
   return WUSH_OK;
 }
 
+KernelFn select_hd_kernel(int fmt, int bs, bool bf16) {
+  if (bs == 32) {
+    switch (fmt) {
+      case kMX: return bf16 ? tq_hd_kernel<32, kMX, true> : tq_hd_kernel<32, kMX, false>;
+      case kI4: return bf16 ? tq_hd_kernel<32, kI4, true> : tq_hd_kernel<32, kI4, false>;
+      case kAmax: return bf16 ? tq_hd_kernel<32, kAmax, true> : tq_hd_kernel<32, kAmax, false>;
+    }
+  } else if (bs == 16) {
+    switch (fmt) {
+      case kNV: return bf16 ? tq_hd_kernel<16, kNV, true> : tq_hd_kernel<16, kNV, false>;
+      case kAmax: return bf16 ? tq_hd_kernel<16, kAmax, true> : tq_hd_kernel<16, kAmax, false>;
+    }
+  }
+  return nullptr;
+}
+
+wush_status launch_hd(int fmt, int bs, bool bf16, int n, int d_in, const void* X, const float* d, float g,
+                      uint8_t* codes, void* scales, uint32_t* amax, hipStream_t stream) {
+  if (n == 0) return WUSH_OK;
+  KernelFn k = select_hd_kernel(fmt, bs, bf16);
+  if (!k) return wush::fail(WUSH_E_UNSUPPORTED, "transform_quant_hd: no kernel for fmt=%d bs=%d", fmt, bs);
+  const int nblk = d_in / bs;
+  const int per_group = kWavesPerGroup * kHdTokens;
+  dim3 grid((nblk + kWave - 1) / kWave, (n + per_group - 1) / per_group);
+  if (grid.y > 65535u) return wush::fail(WUSH_E_SHAPE, "transform_quant_hd: n=%d too large", n);
+  hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, d, n, d_in, g, codes, scales, amax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "transform_quant_hd launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
 // max|T x| over a tensor, written to a device uint (float bits).
-wush_status tensor_amax(int bs, bool bf16, int n, int d_in, const void* X, const float* T, uint32_t* amax_dev,
-                        hipStream_t stream) {
+// (T is a dense [nblk][bs][bs] matrix, or with hd the per-channel scales.)
+wush_status tensor_amax(int bs, bool bf16, int n, int d_in, const void* X, const float* T, bool hd,
+                        uint32_t* amax_dev, hipStream_t stream) {
   hipLaunchKernelGGL(fill_u32, dim3(1), dim3(1), 0, stream, amax_dev, 0u);
+  if (hd) return launch_hd(kAmax, bs, bf16, n, d_in, X, T, 0.0f, nullptr, nullptr, amax_dev, stream);
   return launch(kAmax, bs, bf16, n, d_in, X, T, 0.0f, nullptr, nullptr, amax_dev, stream);
 }
 
-wush_status global_scale(int bs, bool bf16, int n, int d_in, const void* X, const float* T, float* g_out,
+wush_status global_scale(int bs, bool bf16, int n, int d_in, const void* X, const float* T, bool hd, float* g_out,
                          hipStream_t stream) {
   uint32_t* dbuf = nullptr;
   if (hipMalloc(&dbuf, sizeof(uint32_t)) != hipSuccess) return wush::fail(WUSH_E_HIP, "global_scale: hipMalloc failed");
-  wush_status st = tensor_amax(bs, bf16, n, d_in, X, T, dbuf, stream);
+  wush_status st = tensor_amax(bs, bf16, n, d_in, X, T, hd, dbuf, stream);
   uint32_t bits = 0;
   if (st == WUSH_OK) {
     if (hipMemcpyAsync(&bits, dbuf, sizeof bits, hipMemcpyDeviceToHost, stream) != hipSuccess ||
@@ -369,7 +472,7 @@ wush_status wush_nvfp4_global_scale(wush_dtype xdt, int n, int d_in, const void*
   if (n < 1 || d_in < 16 || d_in % 16 != 0)
     return wush::fail(WUSH_E_SHAPE, "wush_nvfp4_global_scale: need n >= 1 and d_in %% 16 == 0");
   if (!wush::aligned16(X)) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale: X must be 16-byte aligned");
-  return global_scale(16, xdt == WUSH_BF16, n, d_in, X, Tx, g_out, static_cast<hipStream_t>(stream));
+  return global_scale(16, xdt == WUSH_BF16, n, d_in, X, Tx, false, g_out, static_cast<hipStream_t>(stream));
 }
 
 wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float* W, const float* Tw, uint8_t* codes,
@@ -381,7 +484,7 @@ wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float*
   if (fmt == WUSH_NVFP4) {
     if (!g_out) return wush::fail(WUSH_E_ARG, "wush_pack_weights: NVFP4 needs g_out");
     if (d_out < 1) return wush::fail(WUSH_E_SHAPE, "wush_pack_weights: NVFP4 needs d_out >= 1");
-    st = global_scale(16, false, d_out, d_in, W, Tw, &g, s);
+    st = global_scale(16, false, d_out, d_in, W, Tw, false, &g, s);
     if (st != WUSH_OK) return st;
     *g_out = g;
   } else if (g_out) {
@@ -389,6 +492,52 @@ wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float*
   }
   const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
   return launch(fk, wush_format_block(fmt), false, d_out, d_in, W, Tw, g, codes, scales, nullptr, s);
+}
+
+wush_status wush_transform_quant_hd(wush_format fmt, wush_dtype xdt, int n, int d_in, const void* X, const float* dx,
+                                    float g, uint8_t* codes, void* scales, void* stream) {
+  wush_status st = check_common("wush_transform_quant_hd", fmt, n, d_in, X, codes, scales);
+  if (st != WUSH_OK) return st;
+  if (xdt != WUSH_F32 && xdt != WUSH_BF16) return wush::fail(WUSH_E_ARG, "wush_transform_quant_hd: bad dtype");
+  if (n > 0 && !dx) return wush::fail(WUSH_E_ARG, "wush_transform_quant_hd: null scales d");
+  if (!wush::aligned16(dx)) return wush::fail(WUSH_E_ARG, "wush_transform_quant_hd: d must be 16-byte aligned");
+  if (fmt == WUSH_NVFP4 && !(g > 0.0f && g < 3.0e38f))
+    return wush::fail(WUSH_E_ARG, "wush_transform_quant_hd: NVFP4 needs a positive finite tensor scale g");
+  const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
+  return launch_hd(fk, wush_format_block(fmt), xdt == WUSH_BF16, n, d_in, X, dx, g, codes, scales, nullptr,
+                   static_cast<hipStream_t>(stream));
+}
+
+wush_status wush_nvfp4_global_scale_hd(wush_dtype xdt, int n, int d_in, const void* X, const float* dx, float* g_out,
+                                       void* stream) {
+  if (!X || !dx || !g_out) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale_hd: null pointer");
+  if (xdt != WUSH_F32 && xdt != WUSH_BF16) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale_hd: bad dtype");
+  if (n < 1 || d_in < 16 || d_in % 16 != 0)
+    return wush::fail(WUSH_E_SHAPE, "wush_nvfp4_global_scale_hd: need n >= 1 and d_in %% 16 == 0");
+  if (!wush::aligned16(X) || !wush::aligned16(dx))
+    return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale_hd: X and d must be 16-byte aligned");
+  return global_scale(16, xdt == WUSH_BF16, n, d_in, X, dx, true, g_out, static_cast<hipStream_t>(stream));
+}
+
+wush_status wush_pack_weights_hd(wush_format fmt, int d_out, int d_in, const float* W, const float* dw, uint8_t* codes,
+                                 void* scales, float* g_out, void* stream) {
+  wush_status st = check_common("wush_pack_weights_hd", fmt, d_out, d_in, W, codes, scales);
+  if (st != WUSH_OK) return st;
+  if (d_out > 0 && !dw) return wush::fail(WUSH_E_ARG, "wush_pack_weights_hd: null scales d");
+  if (!wush::aligned16(dw)) return wush::fail(WUSH_E_ARG, "wush_pack_weights_hd: d must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float g = 0.0f;
+  if (fmt == WUSH_NVFP4) {
+    if (!g_out) return wush::fail(WUSH_E_ARG, "wush_pack_weights_hd: NVFP4 needs g_out");
+    if (d_out < 1) return wush::fail(WUSH_E_SHAPE, "wush_pack_weights_hd: NVFP4 needs d_out >= 1");
+    st = global_scale(16, false, d_out, d_in, W, dw, true, &g, s);
+    if (st != WUSH_OK) return st;
+    *g_out = g;
+  } else if (g_out) {
+    *g_out = 1.0f;
+  }
+  const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
+  return launch_hd(fk, wush_format_block(fmt), false, d_out, d_in, W, dw, g, codes, scales, nullptr, s);
 }
 
 }  // extern "C"

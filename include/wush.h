@@ -101,6 +101,24 @@ wush_status wush_block_moments(int bs, int n, int d_in, const float* X, float* S
 wush_status wush_build_transforms(wush_kind kind, int bs, int d_in, int d_out,
                                   const float* W, const float* Sx, float* Tx, float* Tw);
 
+/* Hadamard-diagonal variant ([WUSH-news], deployment and limitation
+ * paragraphs: the data-aware component approximated by a diagonal matrix).
+ * Reading: the construction above with the moments replaced by their
+ * diagonals.  Per block b and channel i: a_i = sum_o W[o][i]^2 (fp64) and
+ * s_i = Sx_b[i][i]; values below 1e-12 of their block's largest are raised to
+ * that floor (s_i = 1 when the block's s are all zero);
+ *   dx_i = f32(sqrt(sqrt(a_i / s_i)) / sqrt(bs)),
+ *   dw_i = f32(sqrt(sqrt(s_i / a_i)) / sqrt(bs)),
+ * so T_X = H diag(dx) and T_W = H diag(dw) = T_X^{-T} (H the +-1 Sylvester
+ * matrix): among Hadamard-times-diagonal pairs the one that minimises the
+ * proxy loss, (sum_i sqrt(a_i s_i))^2.
+ *   W   host, [d_out][d_in] fp32.      Sx  host, [d_in/bs][bs][bs] fp32.
+ *   dx, dw  host out, [d_in] fp32 each.
+ * Errors: WUSH_E_ARG, WUSH_E_SHAPE (bs not 16/32, d_in % bs, d_out < 1),
+ * WUSH_E_NUMERIC (a block whose weights are all zero). */
+wush_status wush_build_hd(int bs, int d_in, int d_out, const float* W, const float* Sx,
+                          float* dx, float* dw);
+
 /* ------------------------------------------------------------------------
  * Device calls (HIP, gfx950).
  * ---------------------------------------------------------------------- */
@@ -149,6 +167,23 @@ wush_status wush_nvfp4_global_scale(wush_dtype xdt, int n, int d_in, const void*
 wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float* W,
                               const float* Tw, uint8_t* codes, void* scales,
                               float* g_out, void* stream);
+
+/* The Hadamard-diagonal variant of the three calls above (scales from
+ * wush_build_hd, device pointers, [d_in] fp32).  The transform per token (or
+ * weight row) and block is pinned as: v_k = f32(x_k * d_k), then butterfly
+ * stages h = 1, 2, ..., bs/2, each pair (j, j + h) with j in the lower half of
+ * a 2h-aligned group becoming (v_j + v_{j+h}, v_j - v_{j+h}) in fp32 (no
+ * fused multiply-add).  Quantizers, outputs, NVFP4 tensor scale, ownership and
+ * errors are those of wush_transform_quant, wush_nvfp4_global_scale and
+ * wush_pack_weights. */
+wush_status wush_transform_quant_hd(wush_format fmt, wush_dtype xdt, int n, int d_in,
+                                    const void* X, const float* dx, float g,
+                                    uint8_t* codes, void* scales, void* stream);
+wush_status wush_nvfp4_global_scale_hd(wush_dtype xdt, int n, int d_in, const void* X,
+                                       const float* dx, float* g_out, void* stream);
+wush_status wush_pack_weights_hd(wush_format fmt, int d_out, int d_in, const float* W,
+                                 const float* dw, uint8_t* codes, void* scales,
+                                 float* g_out, void* stream);
 
 /* W4A4 matmul, the "FP4 MatMul" of [WUSH-radio]:
  *   Y[m][j] = sum_k dec(A)[m][k] * dec(B)[j][k],  fp32 output, fp32 accumulation.

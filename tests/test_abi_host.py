@@ -187,3 +187,32 @@ def test_dma_kernels_leave_m0_to_their_dma():
             assert re.match(r"buffer_load_dwordx4 .* offen lds$", code[i + 1]), (src, l, code[i + 1])
             n_dma += 1
         assert n_dma > 0, src
+
+
+def test_build_hd_matches_oracle_and_rejects_bad_input():
+    W_, X = random_case(41, 300, 128, 64)
+    for bs in (16, 32):
+        Sx = tr.activation_moments(X, bs).astype(np.float32)
+        Sx[0, 3, 3] = 0.0                         # a dead activation channel is floored, not infinite
+        dx = np.empty(128, np.float32)
+        dw = np.empty(128, np.float32)
+        W.wush_build_hd(bs, W_, Sx, dx, dw)
+        rx, rw, rx64, rw64 = tr.build_hd(W_, Sx, bs)
+        # both round the same fp64 values (summed in different orders) to fp32
+        assert np.allclose(dx, rx64, rtol=4 * 2.0 ** -24, atol=0) and np.allclose(dw, rw64, rtol=4 * 2.0 ** -24, atol=0)
+        assert np.all(np.isfinite(dx)) and np.all(dx > 0)
+    Wz = W_.copy()
+    Wz[:, :32] = 0.0                              # a block with all-zero weights
+    with pytest.raises(W.WushError) as e:
+        W.wush_build_hd(32, Wz, Sx, dx, dw)
+    assert e.value.status == W.WUSH_E_NUMERIC
+    L = W.lib
+    assert L.wush_build_hd(24, 128, 64, None, None, None, None) == W.WUSH_E_ARG
+    buf = np.zeros(4096, np.float32)
+    p = buf.ctypes.data
+    assert L.wush_build_hd(24, 96, 4, p, p, p, p) == W.WUSH_E_SHAPE
+    assert L.wush_build_hd(32, 100, 4, p, p, p, p) == W.WUSH_E_SHAPE
+    assert L.wush_transform_quant_hd(0, 0, 4, 100, None, None, 0.0, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_transform_quant_hd(0, 0, 4, 128, None, None, 0.0, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_pack_weights_hd(0, 4, 128, None, None, None, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_nvfp4_global_scale_hd(0, 4, 128, None, None, None, None) == W.WUSH_E_ARG

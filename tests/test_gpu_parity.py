@@ -90,6 +90,75 @@ def test_transform_quant_edge_cases(fmt, kind):
     assert np.array_equal(gc, rc), np.argwhere(gc != rc)[:8]
 
 
+# Hadamard-diagonal variant: 65 blocks (two 64-block lane groups, the second
+# with one block) and 37 tokens (a ragged last wave) besides small shapes
+SHAPES_HD = {32: [(1, 32), (200, 160), (37, 2080)], 16: [(1, 16), (70, 48), (37, 1040)]}
+
+
+def _gpu_tq_hd(fmt, X, dx, dtype, g):
+    n, d_in = X.shape
+    bs = W.BLOCK[fmt]
+    codes = torch.empty((n, d_in // 2), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((n, d_in // bs), dtype=torch.int16 if fmt == "int4" else torch.uint8, device=DEV)
+    W.wush_transform_quant_hd(fmt, x_dev(X, dtype), to_dev(dx), codes, sc, g=g or 0.0)
+    torch.cuda.synchronize()
+    return host(codes), scales_np(sc, fmt)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_transform_quant_hd_bit_exact(fmt, dtype):
+    bs = W.BLOCK[fmt]
+    for si, (n, d_in) in enumerate(SHAPES_HD[bs]):
+        Wt, X = random_case(300 + si, n, d_in, 48, dtype=dtype)
+        Sx = tr.activation_moments(X, bs).astype(np.float32)
+        dx, _, _, _ = tr.build_hd(Wt, Sx, bs)
+        g = quant.nvfp4_tensor_scale(quant.apply_hd(dx, X, bs)) if fmt == "nvfp4" else None
+        rc, rs = quant.transform_quant_hd(fmt, dx, X, g=g)
+        gc, gs = _gpu_tq_hd(fmt, X, dx, dtype, g)
+        assert np.array_equal(gs, rs), (fmt, dtype, n, d_in, np.argwhere(gs != rs)[:5])
+        assert np.array_equal(gc, rc), (fmt, dtype, n, d_in, np.argwhere(gc != rc)[:5])
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_transform_quant_hd_edge_cases(fmt):
+    d_in = 64
+    X = _edge_inputs(d_in)
+    Wt, Xcal = random_case(6, 50, d_in, 40)
+    bs = W.BLOCK[fmt]
+    dx, _, _, _ = tr.build_hd(Wt, tr.activation_moments(Xcal, bs).astype(np.float32), bs)
+    g = np.float32(0.01) if fmt == "nvfp4" else None
+    with np.errstate(all="ignore"):
+        rc, rs = quant.transform_quant_hd(fmt, dx, X, g=g)
+    gc, gs = _gpu_tq_hd(fmt, X, dx, "f32", g)
+    assert np.array_equal(gs, rs), np.argwhere(gs != rs)[:8]
+    assert np.array_equal(gc, rc), np.argwhere(gc != rc)[:8]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_pack_weights_hd_and_tensor_scale_bit_exact(fmt):
+    bs = W.BLOCK[fmt]
+    Wt, X = random_case(9, 300, 2080 if bs == 32 else 1040, 77)
+    Sx = tr.activation_moments(X, bs).astype(np.float32)
+    dx, dw, _, _ = tr.build_hd(Wt, Sx, bs)
+    g = quant.nvfp4_tensor_scale(quant.apply_hd(dw, Wt, bs)) if fmt == "nvfp4" else None
+    rc, rs = quant.transform_quant_hd(fmt, dw, Wt, g=g)
+    d_out, d_in = Wt.shape
+    codes = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((d_out, d_in // bs), dtype=torch.int16 if fmt == "int4" else torch.uint8, device=DEV)
+    gg = W.wush_pack_weights_hd(fmt, to_dev(Wt), to_dev(dw), codes, sc)
+    torch.cuda.synchronize()
+    if fmt == "nvfp4":
+        assert np.float32(gg).view(np.uint32) == np.float32(g).view(np.uint32)
+        # and the activation-side tensor scale, bf16 input
+        Xb = X[:64]
+        ref = quant.nvfp4_tensor_scale(quant.apply_hd(dx, Xb, bs))
+        ga = W.wush_nvfp4_global_scale_hd(x_dev(Xb, "f32"), to_dev(dx))
+        assert np.float32(ga).view(np.uint32) == np.float32(ref).view(np.uint32)
+    assert np.array_equal(scales_np(sc, fmt), rs)
+    assert np.array_equal(host(codes), rc)
+
+
 def test_transform_quant_empty_batch():
     codes = torch.empty((0, 16), dtype=torch.uint8, device=DEV)
     sc = torch.empty((0, 1), dtype=torch.uint8, device=DEV)
