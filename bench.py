@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--workload", default="qwen3_8b_up",
                     choices=["qwen3_8b_up", "tiny", "square_sweep", "qwen3_14b", "had256"])
     ap.add_argument("--fmt", default=None, help="square_sweep: mxfp4 | nvfp4 | int4")
-    ap.add_argument("--kind", default=None, help="square_sweep: identity | hadamard | wus | wush")
+    ap.add_argument("--kind", default=None,
+                    help="identity | hadamard | wus | wush, or hd (the Hadamard-diagonal variant)")
     ap.add_argument("--batch", type=int, default=1, help="had256: batch 1..16")
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -81,25 +82,35 @@ class Layer:
         # offline: moments and transforms on the host (library C++ builder)
         Sx = np.empty((nblk, self.bs, self.bs), np.float32)
         W.wush_block_moments(self.bs, X, Sx)
-        Tx = np.empty_like(Sx)
-        Tw = np.empty_like(Sx)
-        W.wush_build_transforms(kind, self.bs, Wt if kind in ("wus", "wush") else None,
-                                Sx if kind in ("wus", "wush") else None, Tx, Tw)
-        ident = kind == "identity"
+        self.hd = kind == "hd"
         dev = "cuda"
-        self.Tx = None if ident else torch.from_numpy(Tx).to(dev)
-        Twd = None if ident else torch.from_numpy(Tw).to(dev)
         sdt = torch.int16 if fmt == "int4" else torch.uint8
         Wd = torch.from_numpy(Wt).to(dev)
         wc = torch.empty((self.N, self.K // 2), dtype=torch.uint8, device=dev)
         wsc = torch.empty((self.N, nblk), dtype=sdt, device=dev)
-        self.w_g = W.wush_pack_weights(fmt, Wd, Twd, wc, wsc)
-        del Wd
         if wl.dtype == "bf16":
             xd = torch.from_numpy(bf16_bits(X).view(np.int16)).to(dev).view(torch.bfloat16)
         else:
             xd = torch.from_numpy(X).to(dev)
-        self.x_g = W.wush_nvfp4_global_scale(xd, self.Tx) if fmt == "nvfp4" else 1.0
+        if self.hd:
+            # Hadamard-diagonal variant: per-channel scales instead of block matrices
+            Tx = np.empty(self.K, np.float32)
+            Tw = np.empty(self.K, np.float32)
+            W.wush_build_hd(self.bs, Wt, Sx, Tx, Tw)
+            self.Tx = torch.from_numpy(Tx).to(dev)
+            self.w_g = W.wush_pack_weights_hd(fmt, Wd, torch.from_numpy(Tw).to(dev), wc, wsc)
+            self.x_g = W.wush_nvfp4_global_scale_hd(xd, self.Tx) if fmt == "nvfp4" else 1.0
+        else:
+            Tx = np.empty_like(Sx)
+            Tw = np.empty_like(Sx)
+            W.wush_build_transforms(kind, self.bs, Wt if kind in ("wus", "wush") else None,
+                                    Sx if kind in ("wus", "wush") else None, Tx, Tw)
+            ident = kind == "identity"
+            self.Tx = None if ident else torch.from_numpy(Tx).to(dev)
+            Twd = None if ident else torch.from_numpy(Tw).to(dev)
+            self.w_g = W.wush_pack_weights(fmt, Wd, Twd, wc, wsc)
+            self.x_g = W.wush_nvfp4_global_scale(xd, self.Tx) if fmt == "nvfp4" else 1.0
+        del Wd
         self.X = [xd] + [xd.clone() for _ in range(rotate - 1)]
         self.wc = [wc] + [wc.clone() for _ in range(rotate - 1)]
         self.wsc = [wsc] + [wsc.clone() for _ in range(rotate - 1)]
@@ -116,10 +127,15 @@ class Layer:
     def tq_bytes(self):
         el = self.M * self.K
         sbytes = {"mxfp4": 1.0 / 32, "nvfp4": 1.0 / 16, "int4": 2.0 / 32}[self.fmt]
-        tbytes = 0 if self.kind == "identity" else (self.K // self.bs) * self.bs * self.bs * 4
+        if self.hd:
+            tbytes = self.K * 4
+        else:
+            tbytes = 0 if self.kind == "identity" else (self.K // self.bs) * self.bs * self.bs * 4
         return el * (self.x_elem_bytes + 0.5 + sbytes) + tbytes
 
     def tq_flops(self):
+        if self.hd:   # one product and log2(bs) butterfly adds per element
+            return (1.0 + np.log2(self.bs)) * self.M * self.K
         return 0.0 if self.kind == "identity" else 2.0 * self.bs * self.M * self.K
 
     def gemm_flops(self):
@@ -139,7 +155,10 @@ def run_layer_steps(layers, W, torch, steps, warmup, rotate):
         for li, L in enumerate(layers):
             if ev is not None:
                 ev[li][0].record(stream)
-            W.wush_transform_quant(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
+            if L.hd:
+                W.wush_transform_quant_hd(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
+            else:
+                W.wush_transform_quant(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
             if ev is not None:
                 ev[li][1].record(stream)
             W.wush_w4a4_gemm(L.fmt, L.xc, L.xsc, L.wc[r], L.wsc[r], L.Y, a_g=L.x_g, b_g=L.w_g, ws=L.ws)
@@ -219,24 +238,33 @@ def cpu_baseline(L, target_s):
     ident = L.kind == "identity"
     # the oracle builds its own transforms (untimed)
     Sx = transforms.activation_moments(X, L.bs).astype(np.float32)
-    Tx, Tw, _, _ = transforms.build_transforms(L.kind, Wt, Sx, L.bs)
+    if L.hd:
+        Tx, Tw, _, _ = transforms.build_hd(Wt, Sx, L.bs)
+
+        def tq(T, rows, gg):
+            return quant.transform_quant_hd(L.fmt, T, rows, g=gg)
+    else:
+        Tx, Tw, _, _ = transforms.build_transforms(L.kind, Wt, Sx, L.bs)
+
+        def tq(T, rows, gg):
+            return quant.transform_quant(L.fmt, T, rows, g=gg, identity=ident)
     g = None
     if L.fmt == "nvfp4":
         g = L.x_g
     # size the sample to roughly target_s seconds of work (calibrate on a small run)
     mt = 8
     t0 = time.perf_counter()
-    quant.transform_quant(L.fmt, Tx, X[:mt], g=g, identity=ident)
+    tq(Tx, X[:mt], g)
     per_tok = (time.perf_counter() - t0) / mt
     mt = int(max(8, min(L.M, 0.5 * target_s / max(per_tok, 1e-9))))
     t0 = time.perf_counter()
-    ca, sa = quant.transform_quant(L.fmt, Tx, X[:mt], g=g, identity=ident)
+    ca, sa = tq(Tx, X[:mt], g)
     t_tq = time.perf_counter() - t0
     ns = min(L.N, 1024)
     wg = None
     if L.fmt == "nvfp4":
         wg = L.w_g
-    cw, sw = quant.transform_quant(L.fmt, Tw, Wt[:ns], g=wg, identity=ident)   # untimed prep
+    cw, sw = tq(Tw, Wt[:ns], wg)   # untimed prep
     ms = min(mt, 256)
     t0 = time.perf_counter()
     gemm.w4a4_gemm(L.fmt, ca[:ms], sa[:ms], cw, sw, g, wg)
@@ -326,18 +354,19 @@ def main():
         roof_gemm.update({"bound": "alu", "achieved": round(rescale, 2), "peak": round(VALU_TOPS, 1),
                           "unit": "Top/s", "frac": round(rescale / VALU_TOPS, 4),
                           "int8_TOPS": round(gemm_achieved, 2), "int8_frac": round(gemm_achieved / INT8_TOPS, 4)})
+    tq_name = "wush_transform_quant_hd" if layers[0].hd else "wush_transform_quant"
     t_alu = tq_flops / (VALU_FP32_TFLOPS * 1e12)
     t_hbm = tq_bytes / (HBM_GBPS * 1e9)
     if t_alu > t_hbm:
-        roof_tq = {"kernel": "wush_transform_quant", "bound": "alu", "achieved": round(tq_alu, 2),
+        roof_tq = {"kernel": tq_name, "bound": "alu", "achieved": round(tq_alu, 2),
                    "peak": round(VALU_FP32_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(tq_alu / VALU_FP32_TFLOPS, 4),
-                   "traffic": measured_traffic("wush_transform_quant", wname) if fmt == "mxfp4" else None,
+                   "traffic": measured_traffic(tq_name, wname) if fmt == "mxfp4" else None,
                    "algorithmic_bytes": round(tq_bytes / len(layers)), "avg_us": round(tq_t * 1e6 / len(layers), 2),
                    "hbm_GBps": round(tq_gbps, 1), "hbm_frac": round(tq_gbps / HBM_GBPS, 4)}
     else:
-        roof_tq = {"kernel": "wush_transform_quant", "bound": "hbm", "achieved": round(tq_gbps, 1),
+        roof_tq = {"kernel": tq_name, "bound": "hbm", "achieved": round(tq_gbps, 1),
                    "peak": HBM_GBPS, "unit": "GB/s", "frac": round(tq_gbps / HBM_GBPS, 4),
-                   "traffic": measured_traffic("wush_transform_quant", wname) if fmt == "mxfp4" else None,
+                   "traffic": measured_traffic(tq_name, wname) if fmt == "mxfp4" else None,
                    "algorithmic_bytes": round(tq_bytes / len(layers)), "avg_us": round(tq_t * 1e6 / len(layers), 2)}
     out = {
         "metric": METRIC,
