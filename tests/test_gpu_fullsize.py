@@ -35,33 +35,53 @@ def _layer_check(wl, fmt, kind, Wt, X, n_tok=48, n_w=48, seed=0):
     d_out = Wt.shape[0]
     print(f"[fullsize] {wl.name} {fmt} {kind} n={n} d_in={d_in} d_out={d_out}", flush=True)
     Sx = tr.activation_moments(X, bs).astype(np.float32)
-    Tx, Tw, _, _ = tr.build_transforms(kind, Wt, Sx, bs)
+    hd = kind == "hd"          # the Hadamard-diagonal variant: per-channel scales
+    if hd:
+        Tx, Tw, _, _ = tr.build_hd(Wt, Sx, bs)
+
+        def apply(T, rows):
+            return quant.apply_hd(T, rows, bs)
+
+        def tq(T, rows, g):
+            return quant.transform_quant_hd(fmt, T, rows, g=g)
+    else:
+        Tx, Tw, _, _ = tr.build_transforms(kind, Wt, Sx, bs)
+
+        def apply(T, rows):
+            return quant.apply_transform(T, rows, identity=ident)
+
+        def tq(T, rows, g):
+            return quant.transform_quant(fmt, T, rows, g=g, identity=ident)
     tok = _sample(n, n_tok, seed)
     wrow = _sample(d_out, n_w, seed + 1)
     # NVFP4 scales: activations from a calibration subset (an input), weights over all rows
     g_x = g_w = None
     if fmt == "nvfp4":
         cal = _sample(n, 256, seed + 2)
-        g_x = quant.nvfp4_tensor_scale(quant.apply_transform(Tx, X[cal], identity=ident))
-        g_w = quant.nvfp4_tensor_scale(quant.apply_transform(Tw, Wt, identity=ident))
+        g_x = quant.nvfp4_tensor_scale(apply(Tx, X[cal]))
+        g_w = quant.nvfp4_tensor_scale(apply(Tw, Wt))
 
     # device: the same calls bench.py times
     sdt = torch.int16 if fmt == "int4" else torch.uint8
     xc = torch.empty((n, d_in // 2), dtype=torch.uint8, device=DEV)
     xs = torch.empty((n, d_in // bs), dtype=sdt, device=DEV)
-    W.wush_transform_quant(fmt, x_dev(X, wl.dtype), None if ident else to_dev(Tx), xc, xs, g=g_x or 0.0)
     wc = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=DEV)
     wsc = torch.empty((d_out, d_in // bs), dtype=sdt, device=DEV)
-    gw_dev = W.wush_pack_weights(fmt, to_dev(Wt), None if ident else to_dev(Tw), wc, wsc)
+    if hd:
+        W.wush_transform_quant_hd(fmt, x_dev(X, wl.dtype), to_dev(Tx), xc, xs, g=g_x or 0.0)
+        gw_dev = W.wush_pack_weights_hd(fmt, to_dev(Wt), to_dev(Tw), wc, wsc)
+    else:
+        W.wush_transform_quant(fmt, x_dev(X, wl.dtype), None if ident else to_dev(Tx), xc, xs, g=g_x or 0.0)
+        gw_dev = W.wush_pack_weights(fmt, to_dev(Wt), None if ident else to_dev(Tw), wc, wsc)
     Y = torch.empty((n, d_out), dtype=torch.float32, device=DEV)
     W.wush_w4a4_gemm(fmt, xc, xs, wc, wsc, Y, a_g=g_x or 1.0, b_g=gw_dev)
     torch.cuda.synchronize()
 
     # oracle on the sampled rows
-    rc, rs = quant.transform_quant(fmt, Tx, X[tok], g=g_x, identity=ident)
+    rc, rs = tq(Tx, X[tok], g_x)
     assert np.array_equal(scales_np(xs, fmt)[tok], rs)
     assert np.array_equal(host(xc)[tok], rc)
-    wrc, wrs = quant.transform_quant(fmt, Tw, Wt[wrow], g=g_w, identity=ident)
+    wrc, wrs = tq(Tw, Wt[wrow], g_w)
     assert np.array_equal(scales_np(wsc, fmt)[wrow], wrs)
     assert np.array_equal(host(wc)[wrow], wrc)
     if fmt == "nvfp4":
@@ -97,6 +117,17 @@ def test_fullsize_tiny_layer_with_loss():
 def test_fullsize_qwen3_8b_up():
     wl = CONFIGS["qwen3_8b_up"]
     _layer_check(wl, "mxfp4", "wush", make_weights(wl), make_activations(wl))
+
+
+def test_fullsize_qwen3_8b_up_hd():
+    wl = CONFIGS["qwen3_8b_up"]
+    _layer_check(wl, "mxfp4", "hd", make_weights(wl), make_activations(wl))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_fullsize_square_sweep_hd(fmt):
+    wl = CONFIGS["square_sweep"]
+    _layer_check(wl, fmt, "hd", make_weights(wl), make_activations(wl), n_tok=24, n_w=24)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
