@@ -45,6 +45,8 @@ _SIGS = {
     "wush_nvfp4_global_scale": ([_i, _i, _i, _p, _p, _fp, _p], _i),
     "wush_pack_weights": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
     "wush_build_hd": ([_i, _i, _i, _p, _p, _p, _p], _i),
+    "wush_block_moments_dev_ws_bytes": ([_i, _i, _i], _sz),
+    "wush_block_moments_dev": ([_i, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
     "wush_transform_quant_hd": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _p], _i),
     "wush_nvfp4_global_scale_hd": ([_i, _i, _i, _p, _p, _fp, _p], _i),
     "wush_pack_weights_hd": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
@@ -155,6 +157,22 @@ def wush_pack_weights(fmt, W, Tw, codes, scales, stream=None):
     _check(lib.wush_pack_weights(_fmt(fmt), d_out, d_in, _ptr(W), _ptr(Tw), _ptr(codes), _ptr(scales),
                                  ctypes.byref(g), _stream(stream)), "wush_pack_weights")
     return g.value
+
+
+def wush_block_moments_dev_ws_bytes(bs, n, d_in):
+    return lib.wush_block_moments_dev_ws_bytes(bs, n, d_in)
+
+
+def wush_block_moments_dev(bs, X, Sx, ws=None, stream=None):
+    """X: device [n][d_in] float32 or bfloat16; Sx: device out [d_in/bs][bs][bs] float32."""
+    import torch
+    n, d_in = X.shape
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("X must be float32 or bfloat16")
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    wp, wb = _ws(ws)
+    _check(lib.wush_block_moments_dev(bs, xdt, n, d_in, _ptr(X), _ptr(Sx), wp, wb, _stream(stream)),
+           "wush_block_moments_dev")
 
 
 def wush_transform_quant_hd(fmt, X, dx, codes, scales, g=0.0, stream=None):

@@ -39,6 +39,7 @@ INT8_TOPS = 5000.0          # dense int8 matrix
 VALU_FP32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # vector-ALU lane operations: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
 VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+FP64_TFLOPS = 78.6          # fp64 vector FMA
 # INT4 matmul: per output and 32-group, convert + multiply + fma on the vector ALU
 INT4_RESCALE_OPS = 3
 
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_up",
-                    choices=["qwen3_8b_up", "tiny", "square_sweep", "qwen3_14b", "had256"])
+                    choices=["qwen3_8b_up", "tiny", "square_sweep", "qwen3_14b", "had256", "moments"])
     ap.add_argument("--fmt", default=None, help="square_sweep: mxfp4 | nvfp4 | int4")
     ap.add_argument("--kind", default=None,
                     help="identity | hadamard | wus | wush, or hd (the Hadamard-diagonal variant)")
@@ -319,6 +320,8 @@ def main():
 
     if args.workload == "had256":
         return bench_had256(args, W, torch)
+    if args.workload == "moments":
+        return bench_moments(args, W, torch)
 
     if args.workload == "qwen3_14b":
         wls = [CONFIGS["qwen3_14b_up"], CONFIGS["qwen3_14b_down"]]
@@ -438,6 +441,41 @@ def bench_had256(args, W, torch):
                         "peak": HBM_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_GBPS, 4),
                         "traffic": measured_traffic("wush_had256_gemv_b%d" % B, wl.name),
                         "avg_us": round(ms * 1e3, 2)}}
+    print(json.dumps(out), flush=True)
+
+
+def bench_moments(args, W, torch):
+    """Calibration block moments on the GPU for the Qwen3-8B up-projection's activations (bs 32)."""
+    from synth.gen import CONFIGS, make_activations, bf16_bits
+    wl = CONFIGS["qwen3_8b_up"]
+    X = make_activations(wl)
+    n, d_in = X.shape
+    bs = 32
+    dev = "cuda"
+    xd = torch.from_numpy(bf16_bits(X).view(np.int16)).to(dev).view(torch.bfloat16)
+    Xs = [xd] + [xd.clone() for _ in range(args.rotate - 1)]
+    Sx = torch.empty((d_in // bs, bs, bs), dtype=torch.float32, device=dev)
+    ws = torch.empty(W.wush_block_moments_dev_ws_bytes(bs, n, d_in), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        W.wush_block_moments_dev(bs, Xs[i % args.rotate], Sx, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        W.wush_block_moments_dev(bs, Xs[i % args.rotate], Sx, ws=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 2.0 * n * d_in * bs            # the full bs x bs product per block and token
+    tflops = flops / (ms / 1e3) / 1e12
+    out = {"metric": "calibration block moments TFLOP/s (fp64 accumulation)", "value": round(tflops, 3),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+           "data": "synthetic", "config": {"workload": wl.name + "-moments", "tokens": n, "d_in": d_in, "bs": bs},
+           "roofline": {"kernel": "wush_block_moments_dev", "bound": "alu", "achieved": round(tflops, 3),
+                        "peak": FP64_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP64_TFLOPS, 4),
+                        "traffic": None, "avg_us": round(ms * 1e3, 2)}}
     print(json.dumps(out), flush=True)
 
 

@@ -83,6 +83,22 @@ int wush_format_block(wush_format fmt);
  * Errors: WUSH_E_ARG (null), WUSH_E_SHAPE (n < 1, bs not 16/32, d_in % bs). */
 wush_status wush_block_moments(int bs, int n, int d_in, const float* X, float* Sx);
 
+/* The same moments on the GPU (device pointers, stream-ordered): the step
+ * before the builder, [WUSH-news] deployment paragraph (moments from
+ * calibration data; per-block work in parallel).  Products are formed exactly
+ * in fp64 and summed in fp64 per chunk of up to 256 tokens, the chunks in
+ * order, then divided by n and rounded once to fp32; Sx is exactly symmetric.
+ * Agrees with wush_block_moments up to fp64 summation order.
+ *   X   device, [n][d_in] fp32 or bf16 (xdt), 16-byte aligned.
+ *   Sx  device out, [d_in/bs][bs][bs] fp32.
+ *   ws  device scratch of wush_block_moments_dev_ws_bytes(bs, n, d_in) bytes
+ *       (fp64 chunk partials, 16-byte aligned), or NULL (taken from the
+ *       default memory pool for the call).
+ * Errors: WUSH_E_ARG, WUSH_E_SHAPE (n < 1, bs not 16/32, d_in % bs), WUSH_E_HIP. */
+size_t wush_block_moments_dev_ws_bytes(int bs, int n, int d_in);
+wush_status wush_block_moments_dev(int bs, wush_dtype xdt, int n, int d_in, const void* X,
+                                   float* Sx, void* ws, size_t ws_bytes, void* stream);
+
 /* Per-block transform pair, [WUSH-news] construction paragraph (Cholesky
  * factor of weight statistics, U and S of an SVD, Hadamard) and deployment
  * paragraph (per block, in parallel).  For every block b:

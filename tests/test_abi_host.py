@@ -216,3 +216,15 @@ def test_build_hd_matches_oracle_and_rejects_bad_input():
     assert L.wush_transform_quant_hd(0, 0, 4, 128, None, None, 0.0, None, None, None) == W.WUSH_E_ARG
     assert L.wush_pack_weights_hd(0, 4, 128, None, None, None, None, None, None) == W.WUSH_E_ARG
     assert L.wush_nvfp4_global_scale_hd(0, 4, 128, None, None, None, None) == W.WUSH_E_ARG
+
+
+def test_block_moments_dev_checks_and_workspace_size():
+    L = W.lib
+    # 300 tokens: 2 chunks of up to 256; 5000: 20; 20000: capped at 64
+    assert L.wush_block_moments_dev_ws_bytes(32, 300, 128) == 2 * 128 * 32 * 8
+    assert L.wush_block_moments_dev_ws_bytes(16, 5000, 64) == 20 * 64 * 16 * 8
+    assert L.wush_block_moments_dev_ws_bytes(32, 20000, 64) == 64 * 64 * 32 * 8
+    assert L.wush_block_moments_dev_ws_bytes(24, 300, 96) == 0
+    assert L.wush_block_moments_dev(24, 0, 10, 96, None, None, None, 0, None) == W.WUSH_E_SHAPE
+    assert L.wush_block_moments_dev(32, 0, 0, 64, None, None, None, 0, None) == W.WUSH_E_SHAPE
+    assert L.wush_block_moments_dev(32, 0, 10, 64, None, None, None, 0, None) == W.WUSH_E_ARG

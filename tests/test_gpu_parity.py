@@ -159,6 +159,28 @@ def test_pack_weights_hd_and_tensor_scale_bit_exact(fmt):
     assert np.array_equal(host(codes), rc)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_block_moments_on_device(bs, dtype):
+    # 1, 300 (two chunks, the second short) and 5000 tokens (20 chunks)
+    for n in (1, 300, 5000):
+        _, X = random_case(60 + n, n, 4 * bs + 64, 8, dtype=dtype)
+        d_in = X.shape[1]
+        Sx = torch.full((d_in // bs, bs, bs), np.nan, dtype=torch.float32, device=DEV)
+        ws = torch.empty(W.wush_block_moments_dev_ws_bytes(bs, n, d_in), dtype=torch.uint8, device=DEV)
+        for w in (None, ws):
+            W.wush_block_moments_dev(bs, x_dev(X, dtype), Sx, ws=w)
+            torch.cuda.synchronize()
+            got = host(Sx)
+            ref = tr.activation_moments(X, bs)
+            assert np.array_equal(got, got.transpose(0, 2, 1))
+            assert np.allclose(got, ref, rtol=2e-7, atol=1e-7 * np.abs(ref).max()), (n, np.abs(got - ref).max())
+            # and the host library's fp64 moments up to summation order: within one fp32 ulp
+            hx = np.empty_like(got)
+            W.wush_block_moments(bs, X, hx)
+            assert np.all(np.abs(got - hx) <= np.spacing(np.abs(hx)))
+
+
 def test_transform_quant_empty_batch():
     codes = torch.empty((0, 16), dtype=torch.uint8, device=DEV)
     sc = torch.empty((0, 1), dtype=torch.uint8, device=DEV)
