@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kVec) void had256_rotate_kernel(const float* __rest
 constexpr int kGemvWaves = 16;     // K split inside a workgroup: wave w takes chunks w, w + 16, ...
 constexpr int kGemvTiles = 4;      // 16-row MFMA tiles (row blocks) per workgroup
 constexpr int kGemvRows = kBlockRows * kGemvTiles;
-constexpr int kFusedBatch = 1;     // batches up to this size rotate their activations inside the GEMV
+constexpr int kFusedBatch = 4;     // batches up to this size rotate their activations inside the GEMV
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -362,9 +362,11 @@ template <int B, bool kFused>
 __global__ __launch_bounds__(64 * kGemvWaves) void had256_gemv_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ act, const float4* __restrict__ stats,
     const uint8_t* __restrict__ packed, float* __restrict__ y, int nb, int d_out, int d_in) {
-  static_assert(!kFused || B == 1, "the in-kernel rotation serves one batch row");
+  static_assert(!kFused || B <= kFusedBatch, "the in-kernel rotation serves up to kFusedBatch rows");
   // B is the compiled batch capacity; nb <= B rows of x / y are real.
-  __shared__ __attribute__((aligned(16))) int8_t act_l[kFused ? kGemvWaves : 1][2][4][4][16];   // [.][hi/lo][g][t][p]
+  __shared__ __attribute__((aligned(16))) int8_t act_l[kFused ? kGemvWaves : 1][2][4][4][B][16];   // [.][hi/lo][g][t][n][p]
+  __shared__ float sg_l[kFused && B > 1 ? kGemvWaves : 1][B];
+  __shared__ int2 sum_l[kFused && B > 1 ? kGemvWaves : 1][B];
   __shared__ float red[kGemvWaves][kGemvRows][B];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: chunk addresses stay scalar
@@ -388,9 +390,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void had256_gemv_kernel(
     // wait a full drain): blocks past the last re-read the last block, whose
     // outputs are never stored.
     Act a;
-    uint2 xv;
+    uint2 xv[kFused ? B : 1];
     if constexpr (kFused) {
-      xv = *reinterpret_cast<const uint2*>(x + c * kVec + 16 * r16 + 4 * g);
+#pragma unroll
+      for (int b = 0; b < B; ++b)   // rows past nb repeat row nb - 1
+        xv[b] = *reinterpret_cast<const uint2*>(x + static_cast<size_t>(min(b, nb - 1)) * d_in + c * kVec + 16 * r16 +
+                                                4 * g);
     } else {
       load_act(act, act_lo, stats, c, nv, nb, r16, g, a);
     }
@@ -411,22 +416,40 @@ __global__ __launch_bounds__(64 * kGemvWaves) void had256_gemv_kernel(
     // keep every load above issued before any work that waits on one of them
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kFused) {
-      const Split sp = rotate_split(xv, lane);
-      // element 64 g + 16 e + r16 is byte r16 of operand (t = e, g)
+      Split sp0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        act_l[wave][0][g][e][r16] = static_cast<int8_t>(sp.hi >> (8 * e));
-        act_l[wave][1][g][e][r16] = static_cast<int8_t>(sp.lo >> (8 * e));
+      for (int b = 0; b < B; ++b) {
+        const Split sp = rotate_split(xv[b], lane);
+        // element 64 g + 16 e + r16 of row b is byte r16 of operand (t = e, g), column b
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          act_l[wave][0][g][e][b][r16] = static_cast<int8_t>(sp.hi >> (8 * e));
+          act_l[wave][1][g][e][b][r16] = static_cast<int8_t>(sp.lo >> (8 * e));
+        }
+        if constexpr (B == 1) {
+          sp0 = sp;
+        } else if (lane == 0) {   // sigma and the sums are wave-uniform
+          sg_l[wave][b] = sp.sigma;
+          sum_l[wave][b] = make_int2(sp.sum_hi, sp.sum_lo);
+        }
       }
       wave_lds_sync();
+      const int n = min(r16, nb - 1);   // lanes past the batch read row nb - 1; never stored
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        a.ah[t] = *reinterpret_cast<const v4i*>(&act_l[wave][0][g][t][0]);
-        a.al[t] = *reinterpret_cast<const v4i*>(&act_l[wave][1][g][t][0]);
+        a.ah[t] = *reinterpret_cast<const v4i*>(&act_l[wave][0][g][t][n][0]);
+        a.al[t] = *reinterpret_cast<const v4i*>(&act_l[wave][1][g][t][n][0]);
       }
-      a.sg = sp.sigma;
-      a.sum_hi = sp.sum_hi;
-      a.sum_lo = sp.sum_lo;
+      if constexpr (B == 1) {
+        a.sg = sp0.sigma;
+        a.sum_hi = sp0.sum_hi;
+        a.sum_lo = sp0.sum_lo;
+      } else {
+        a.sg = sg_l[wave][n];
+        const int2 sm = sum_l[wave][n];
+        a.sum_hi = sm.x;
+        a.sum_lo = sm.y;
+      }
     }
     const float f = a.sg * (1.0f / 2048.0f);
 #pragma unroll
@@ -517,7 +540,10 @@ wush_status wush_had256_gemv(int batch, int d_out, int d_in, const uint16_t* x, 
   if (ws && !wush::aligned16(ws)) return wush::fail(WUSH_E_ARG, "wush_had256_gemv: workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch <= kFusedBatch) {
-    launch_gemv<kFusedBatch, true>(batch, d_out, d_in, x, nullptr, nullptr, packed, y, s);
+    if (batch == 1)
+      launch_gemv<1, true>(batch, d_out, d_in, x, nullptr, nullptr, packed, y, s);
+    else
+      launch_gemv<kFusedBatch, true>(batch, d_out, d_in, x, nullptr, nullptr, packed, y, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "wush_had256_gemv launch: %s", hipGetErrorString(e));
     return WUSH_OK;
@@ -536,10 +562,7 @@ wush_status wush_had256_gemv(int batch, int d_out, int d_in, const uint16_t* x, 
   int8_t* act = reinterpret_cast<int8_t*>(wsp);
   float4* stats = reinterpret_cast<float4*>(wsp + act_bytes);
   hipLaunchKernelGGL(had256_prep_kernel, dim3(nv, batch), dim3(64), 0, s, x, batch, d_in, act, stats);
-  if (batch <= 4)
-    launch_gemv<4, false>(batch, d_out, d_in, x, act, stats, packed, y, s);
-  else
-    launch_gemv<16, false>(batch, d_out, d_in, x, act, stats, packed, y, s);
+  launch_gemv<16, false>(batch, d_out, d_in, x, act, stats, packed, y, s);
   const hipError_t fe = ws ? hipSuccess : hipFreeAsync(wsp, s);
   if (fe != hipSuccess) return wush::fail(WUSH_E_HIP, "wush_had256_gemv scratch free: %s", hipGetErrorString(fe));
   hipError_t e = hipGetLastError();

@@ -278,8 +278,8 @@ wush_status wush_had256_pack_weights(int d_out, int d_in, const float* W,
  *   ws      device scratch of at least wush_had256_gemv_ws_bytes(batch, d_in)
  *           bytes (16-byte aligned), or NULL (taken from the default memory
  *           pool per call, as for wush_w4a4_gemm); calls sharing a ws must be
- *           ordered on one stream.  Batch 1 needs none (size 0): its
- *           activations are rotated and split inside the GEMV kernel.
+ *           ordered on one stream.  Batches up to 4 need none (size 0):
+ *           their activations are rotated and split inside the GEMV kernel.
  * Errors: WUSH_E_SHAPE (batch not in 1..16, d_in % 256, d_in > 2^24),
  * WUSH_E_ARG, WUSH_E_HIP. */
 size_t wush_had256_gemv_ws_bytes(int batch, int d_in);

@@ -55,12 +55,13 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert L.wush_had256_gemv(1, 4, (1 << 24) + 256, None, None, None, None, 0, None) == W.WUSH_E_SHAPE
     assert L.wush_had256_gemv(1, 4, 256, None, None, None, None, 0, None) == W.WUSH_E_ARG
     # workspace sizes (host-side arithmetic only)
-    assert L.wush_had256_gemv_ws_bytes(4, 4096) == 2 * 4 * 4096 + 4 * 16 * 16
+    assert L.wush_had256_gemv_ws_bytes(5, 4096) == 2 * 5 * 4096 + 5 * 16 * 16
+    assert L.wush_had256_gemv_ws_bytes(4, 4096) == 0    # batches up to 4 rotate inside the GEMV
     assert L.wush_had256_packed_bytes(37, 768) == 3 * 3 * 1568       # rows padded to 16-row blocks
     assert L.wush_had256_packed_bytes(14336, 4096) == 896 * 16 * 1568
     assert L.wush_had256_packed_bytes(4, 100) == 0
     assert L.wush_had256_gemv_ws_bytes(0, 4096) == 0
-    assert L.wush_had256_gemv_ws_bytes(1, 4096) == 0    # batch 1 rotates inside the GEMV
+    assert L.wush_had256_gemv_ws_bytes(1, 4096) == 0
     assert L.wush_w4a4_gemm_ws_bytes(0, 4096, 12288, 4096) == (16 + 48) * 16 * 2048
     assert L.wush_w4a4_gemm_ws_bytes(0, 4096, 12288, 128) == 0
     assert L.wush_w4a4_gemm_ws_bytes(1, 4096, 12288, 4096) == (16 + 48) * 16 * 8192
