@@ -42,6 +42,7 @@ _SIGS = {
     "wush_block_moments": ([_i, _i, _i, _p, _p], _i),
     "wush_build_transforms": ([_i, _i, _i, _i, _p, _p, _p, _p], _i),
     "wush_transform_quant": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _p], _i),
+    "wush_transform_apply": ([_i, _i, _i, _i, _p, _p, _p, _p], _i),
     "wush_nvfp4_global_scale": ([_i, _i, _i, _p, _p, _fp, _p], _i),
     "wush_pack_weights": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
     "wush_build_hd": ([_i, _i, _i, _p, _p, _p, _p], _i),
@@ -138,6 +139,17 @@ def wush_transform_quant(fmt, X, Tx, codes, scales, g=0.0, stream=None):
         raise TypeError("X must be float32 or bfloat16")
     _check(lib.wush_transform_quant(_fmt(fmt), xdt, n, d_in, _ptr(X), _ptr(Tx), float(g), _ptr(codes),
                                     _ptr(scales), _stream(stream)), "wush_transform_quant")
+
+
+def wush_transform_apply(X, Tx, Y, stream=None):
+    """Y = T x per block (fp32, the transform wush_transform_quant quantizes).  Tx: [nblk][bs][bs]."""
+    import torch
+    n, d_in = X.shape
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("X must be float32 or bfloat16")
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    _check(lib.wush_transform_apply(xdt, Tx.shape[-1], n, d_in, _ptr(X), _ptr(Tx), _ptr(Y), _stream(stream)),
+           "wush_transform_apply")
 
 
 def wush_nvfp4_global_scale(X, Tx, stream=None):

@@ -32,6 +32,10 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", f"-I{INCLUDE}"]
+# per-source extras: the transform kernels read each MFMA result with the
+# vector ALU right away, so their accumulators live in ordinary VGPRs (in
+# AGPRs every value would cost a v_accvgpr_read first)
+HIP_EXTRA = {"transform_quant.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -50,7 +54,7 @@ def build(verbose=False):
     jobs = []
     for s in HIP_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, s), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *HIP_EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", obj])
     for s in CXX_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
         jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", obj])

@@ -40,6 +40,7 @@ VALU_FP32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # vector-ALU lane operations: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
 VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 FP64_TFLOPS = 78.6          # fp64 vector FMA
+MFMA_FP32_TFLOPS = 157.3    # dense fp32 matrix (the dense transforms run on v_mfma_f32_16x16x4_f32)
 # INT4 matmul: per output and 32-group, convert + multiply + fma on the vector ALU
 INT4_RESCALE_OPS = 3
 
@@ -358,11 +359,13 @@ def main():
                           "unit": "Top/s", "frac": round(rescale / VALU_TOPS, 4),
                           "int8_TOPS": round(gemm_achieved, 2), "int8_frac": round(gemm_achieved / INT8_TOPS, 4)})
     tq_name = "wush_transform_quant_hd" if layers[0].hd else "wush_transform_quant"
-    t_alu = tq_flops / (VALU_FP32_TFLOPS * 1e12)
+    # dense transforms: fp32 matrix cores; the diagonal variant: vector ALU
+    tq_peak, tq_bound = (VALU_FP32_TFLOPS, "alu") if layers[0].hd else (MFMA_FP32_TFLOPS, "mfma")
+    t_alu = tq_flops / (tq_peak * 1e12)
     t_hbm = tq_bytes / (HBM_GBPS * 1e9)
     if t_alu > t_hbm:
-        roof_tq = {"kernel": tq_name, "bound": "alu", "achieved": round(tq_alu, 2),
-                   "peak": round(VALU_FP32_TFLOPS, 1), "unit": "TFLOP/s", "frac": round(tq_alu / VALU_FP32_TFLOPS, 4),
+        roof_tq = {"kernel": tq_name, "bound": tq_bound, "achieved": round(tq_alu, 2),
+                   "peak": round(tq_peak, 1), "unit": "TFLOP/s", "frac": round(tq_alu / tq_peak, 4),
                    "traffic": measured_traffic(tq_name, wname) if fmt == "mxfp4" else None,
                    "algorithmic_bytes": round(tq_bytes / len(layers)), "avg_us": round(tq_t * 1e6 / len(layers), 2),
                    "hbm_GBps": round(tq_gbps, 1), "hbm_frac": round(tq_gbps / HBM_GBPS, 4)}

@@ -154,7 +154,7 @@ wush_status wush_build_hd(int bs, int d_in, int d_out, const float* W, const flo
  *   sign bit.  A block with a NaN/Inf value gets the format's NaN scale (0xFF,
  *   0x7F, 0x7E00) and all-zero codes.
  *   X       device, [n][d_in] fp32 or bf16 (xdt).
- *   Tx      device, [d_in/bs][bs][bs] fp32, or NULL for identity.
+ *   Tx      device, [d_in/bs][bs][bs] fp32, or NULL for identity (16-byte aligned).
  *   g       NVFP4 per-tensor fp32 scale (> 0, finite); ignored otherwise.
  *   codes   device out, [n][d_in/2] bytes.
  *   scales  device out, [n][d_in/bs]: uint8 (MXFP4, NVFP4) or uint16 fp16 bits (INT4).
@@ -162,6 +162,16 @@ wush_status wush_build_hd(int bs, int d_in, int d_out, const float* W, const flo
 wush_status wush_transform_quant(wush_format fmt, wush_dtype xdt, int n, int d_in,
                                  const void* X, const float* Tx, float g,
                                  uint8_t* codes, void* scales, void* stream);
+
+/* The transform of wush_transform_quant without the quantizer: Y = T x per
+ * token and block ([WUSH-news] deployment paragraph), with the same pinned
+ * fp32 FMA chain, so Y holds exactly the values the quantizers see.
+ *   bs      16 or 32.          X   device, [n][d_in] fp32 or bf16 (xdt).
+ *   Tx      device, [d_in/bs][bs][bs] fp32 (not NULL, 16-byte aligned).
+ *   Y       device out, [n][d_in] fp32.  X and Y 16-byte aligned.
+ * Errors: WUSH_E_ARG, WUSH_E_SHAPE, WUSH_E_HIP. */
+wush_status wush_transform_apply(wush_dtype xdt, int bs, int n, int d_in, const void* X,
+                                 const float* Tx, float* Y, void* stream);
 
 /* NVFP4 per-tensor scale of transformed data: g = f32(max|T x| / 2688)
  * (2688 = 6 * 448, the largest E2M1 value times the largest E4M3 value).

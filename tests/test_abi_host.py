@@ -47,6 +47,10 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert L.wush_transform_quant(0, 0, 4, 63, None, None, 0.0, None, None, None) == W.WUSH_E_SHAPE
     assert L.wush_transform_quant(9, 0, 4, 64, None, None, 0.0, None, None, None) == W.WUSH_E_ARG
     assert b"format" in L.wush_last_error()
+    assert L.wush_transform_apply(0, 24, 4, 64, None, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_transform_apply(0, 32, 4, 48, None, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_transform_apply(0, 32, 4, 64, None, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_transform_apply(0, 32, 0, 64, None, None, None, None) == W.WUSH_OK
     assert L.wush_w4a4_gemm(0, 4, 4, 100, None, None, 1.0, None, None, 1.0, None, None, 0, None) == W.WUSH_E_SHAPE
     assert L.wush_w4a4_gemm(0, 4, 4, 128, None, None, 1.0, None, None, 1.0, None, None, 0, None) == W.WUSH_E_ARG
     assert L.wush_w4a4_gemm(0, 0, 4, 128, None, None, 1.0, None, None, 1.0, None, None, 0, None) == W.WUSH_E_SHAPE

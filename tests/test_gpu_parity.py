@@ -12,7 +12,7 @@ import torch
 
 import aware_block_transforms_amd as W
 from oracle import quant, transforms as tr, gemm as og, had256 as oh
-from synth.gen import random_case
+from synth.gen import random_case, bf16_round
 from gpu_util import DEV, to_dev, x_dev, host, scales_np, gemm_close
 
 pytestmark = pytest.mark.gpu
@@ -54,6 +54,56 @@ def test_transform_quant_bit_exact(fmt, kind, dtype):
         gc, gs = _gpu_tq(fmt, X, Tx, dtype, g, kind == "identity")
         assert np.array_equal(gs, rs), (fmt, kind, dtype, n, d_in, np.argwhere(gs != rs)[:5])
         assert np.array_equal(gc, rc), (fmt, kind, dtype, n, d_in, np.argwhere(gc != rc)[:5])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bs", [32, 16])
+def test_transform_apply_bit_exact(bs, dtype):
+    # the transformed values themselves, bit for bit (signed zeros included)
+    fmt = "mxfp4" if bs == 32 else "nvfp4"
+    for si, (n, d_in) in enumerate(SHAPES32 if bs == 32 else SHAPES16):
+        Wt, X = random_case(300 + si, n, d_in, 40, dtype=dtype)
+        for kind in ("hadamard", "wus", "wush"):
+            Tx, _, _, _, _ = _oracle_tq(fmt, kind, X, Wt)
+            Y = torch.empty((n, d_in), dtype=torch.float32, device=DEV)
+            W.wush_transform_apply(x_dev(X, dtype), to_dev(Tx), Y)
+            torch.cuda.synchronize()
+            ref = quant.apply_transform(Tx, X)
+            assert np.array_equal(host(Y).view(np.uint32), ref.view(np.uint32)), (bs, dtype, kind, n, d_in)
+
+
+def _adversarial(rng, shape, lo, hi):
+    # random signs and exponents spread over [lo, hi): wide dynamic range, so
+    # that partial sums cancel and round differently in any other order
+    e = rng.integers(lo, hi, size=shape)
+    m = 1.0 + rng.random(shape)
+    return (np.where(rng.random(shape) < 0.5, -1.0, 1.0) * np.ldexp(m, e)).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bs", [32, 16])
+def test_transform_apply_adversarial(bs, dtype):
+    rng = np.random.default_rng([11, bs])
+    n, d_in = 96, 8 * bs
+    nblk = d_in // bs
+    T = _adversarial(rng, (nblk, bs, bs), -30, 30)
+    T[1] = _adversarial(rng, (bs, bs), -8, 8)
+    T[1, :, bs // 2:] = -T[1, :, :bs // 2] * np.float32(1 + 2.0 ** -20)    # near-total cancellation
+    X = _adversarial(rng, (n, d_in), -30, 30)
+    X[:16] = _adversarial(rng, (16, d_in), -149, -120)                     # subnormal and tiny inputs
+    X[16:32, : d_in // 2] = np.float32(0.0)
+    X[16:32, d_in // 2:] = np.float32(-0.0)                               # signed zeros
+    X[32:48] = _adversarial(rng, (16, d_in), -8, 8)
+    X[32:48, bs // 2: bs] = X[32:48, : bs // 2]                            # pairs with the cancelling block
+    if dtype == "bf16":
+        X = bf16_round(X)
+    Y = torch.empty((n, d_in), dtype=torch.float32, device=DEV)
+    W.wush_transform_apply(x_dev(X, dtype), to_dev(T), Y)
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        ref = quant.apply_transform(T, X)
+    assert np.isfinite(ref).all()
+    assert np.array_equal(host(Y).view(np.uint32), ref.view(np.uint32)), np.argwhere(host(Y) != ref)[:8]
 
 
 def _edge_inputs(d_in):
