@@ -153,6 +153,47 @@ def build_transforms(kind, Wt, Sx, bs):
 
 
 # ---------------------------------------------------------------------------
+# Shared-transform variant.  The news article's paragraph on deployment
+# limits proposes sharing one transform among similar blocks.  The pages give
+# no rule for grouping or for building the shared matrix.  Reading used here:
+# the caller assigns every block a group id; a group's matrix is the
+# construction above applied to the group's summed moments
+#     A_G = sum_{b in G} W_b W_b^T,   B_G = sum_{b in G} B_b,
+# i.e. the group's blocks are treated as further samples of one block.  It
+# minimises J(T; A_G, B_G), which bounds the group's summed per-block proxies
+# sum_b J(T; A_b, B_b) from above (a sum of products of non-negative terms is
+# at most the product of the sums).  T_X = T_W^{-T} still holds per group, so
+# the unquantized product is unchanged.
+
+def build_shared(kind, Wt, Sx, bs, group, ngroups):
+    """Per-group (Tx, Tw) as float32 [ngroups][bs][bs] and the fp64 versions.
+
+    group: [nblk] ints in [0, ngroups); every group must own a block.
+    """
+    d_in = np.asarray(Wt).shape[1]
+    nblk = d_in // bs
+    group = np.asarray(group)
+    if group.shape != (nblk,) or group.min() < 0 or group.max() >= ngroups:
+        raise ValueError("group ids must be one per block, in [0, ngroups)")
+    if len(np.unique(group)) != ngroups:
+        raise ValueError("every group must own at least one block")
+    A = weight_moments(Wt, bs) if kind in ("wus", "wush") else None
+    Tx64 = np.empty((ngroups, bs, bs))
+    Tw64 = np.empty((ngroups, bs, bs))
+    for gi in range(ngroups):
+        members = np.flatnonzero(group == gi)
+        Ag = A[members].sum(axis=0) if A is not None else None
+        Bg = np.asarray(Sx, dtype=np.float64)[members].sum(axis=0) if Sx is not None else None
+        Tx64[gi], Tw64[gi] = block_transform(kind, Ag, Bg, bs)
+    return Tx64.astype(np.float32), Tw64.astype(np.float32), Tx64, Tw64
+
+
+def expand_shared(Tg, group):
+    """Per-block matrices [nblk][bs][bs] from the per-group ones."""
+    return np.asarray(Tg)[np.asarray(group)]
+
+
+# ---------------------------------------------------------------------------
 # Hadamard-diagonal variant.  The news article's paragraphs on deployment and
 # on limitations propose approximating the data-aware component by a diagonal
 # matrix.  Reading used here: keep the orthonormal Hadamard and replace

@@ -244,3 +244,72 @@ def test_hd_floors_and_zero_blocks():
     assert np.allclose(dx0, np.sqrt(np.sqrt(np.maximum(a, 4e-12))) / np.sqrt(32))
     with pytest.raises(np.linalg.LinAlgError):
         tr.hd_block_scales(np.zeros(32), bb, 32)
+
+
+# ---------------------------------------------------------------------------
+# shared-transform variant
+
+def test_shared_with_one_block_per_group_is_the_per_block_build():
+    Wt, X = random_case(41, 96, 128, 40)
+    bs = 32
+    Sx = tr.activation_moments(X, bs)
+    for kind in ("wus", "wush"):
+        _, _, tx, tw = tr.build_transforms(kind, Wt, Sx, bs)
+        _, _, sx, sw = tr.build_shared(kind, Wt, Sx, bs, np.arange(4), 4)
+        assert np.array_equal(sx, tx) and np.array_equal(sw, tw)
+
+
+def test_shared_is_invariant_to_duplicated_blocks():
+    # k copies of one block's data: A_G = k A_b and B_G = k B_b, and the
+    # construction is unchanged by a common positive scale of A and B
+    rng = np.random.default_rng(42)
+    bs, k = 16, 3
+    Wb = rng.standard_normal((40, bs))
+    Xb = rng.standard_normal((60, bs)) * np.linspace(0.5, 4.0, bs)
+    Wt = np.tile(Wb, (1, k)).astype(np.float32)
+    X = np.tile(Xb, (1, k)).astype(np.float32)
+    Sx = tr.activation_moments(X, bs)
+    _, _, one_x, one_w = tr.build_transforms("wush", Wt[:, :bs], Sx[:1], bs)
+    _, _, sx, sw = tr.build_shared("wush", Wt, Sx, bs, np.zeros(k, dtype=int), 1)
+    assert np.allclose(sx[0], one_x[0], rtol=1e-9, atol=1e-12)
+    assert np.allclose(sw[0], one_w[0], rtol=1e-9, atol=1e-12)
+
+
+def test_shared_pair_is_inverse_transpose_and_keeps_the_product():
+    Wt, X = random_case(43, 80, 192, 24)
+    bs = 32
+    Sx = tr.activation_moments(X, bs)
+    group = np.array([0, 1, 0, 2, 1, 0])
+    _, _, gx, gw = tr.build_shared("wush", Wt, Sx, bs, group, 3)
+    for gi in range(3):
+        assert np.allclose(gw[gi].T @ gx[gi], np.eye(bs), atol=1e-9)
+    Tx, Tw = tr.expand_shared(gx, group), tr.expand_shared(gw, group)
+    W64, X64 = Wt.astype(np.float64), X.astype(np.float64)
+    Y = np.zeros((X.shape[0], Wt.shape[0]))
+    for b in range(len(group)):
+        sl = slice(b * bs, (b + 1) * bs)
+        Y += (X64[:, sl] @ Tx[b].T) @ (W64[:, sl] @ Tw[b].T).T
+    assert np.allclose(Y, X64 @ W64.T, rtol=1e-9, atol=1e-9)
+
+
+def test_shared_group_minimises_its_pooled_proxy():
+    # the group's matrix beats the members' own matrices on the pooled moments
+    Wt, X = random_case(44, 120, 96, 48)
+    bs = 32
+    Sx = tr.activation_moments(X, bs).astype(np.float64)
+    A = tr.weight_moments(Wt, bs)
+    # J takes the weight-side matrix T_W (the activation side is T_W^{-T})
+    _, _, _, gw = tr.build_shared("wush", Wt, Sx, bs, np.zeros(3, dtype=int), 1)
+    _, _, _, pw = tr.build_transforms("wush", Wt, Sx, bs)
+    J = lambda T: tr.proxy_loss(T, A.sum(axis=0), Sx.sum(axis=0))
+    assert all(J(gw[0]) < J(pw[b]) * (1 - 1e-9) for b in range(3))
+    assert J(gw[0]) < J(tr.hadamard_normalized(bs))
+
+
+def test_shared_rejects_bad_groups():
+    Wt, X = random_case(45, 40, 64, 8)
+    Sx = tr.activation_moments(X, 32)
+    with pytest.raises(ValueError):
+        tr.build_shared("wush", Wt, Sx, 32, np.array([0, 2]), 2)
+    with pytest.raises(ValueError):
+        tr.build_shared("wush", Wt, Sx, 32, np.array([0, 0]), 2)
