@@ -43,6 +43,10 @@ _SIGS = {
     "wush_build_transforms": ([_i, _i, _i, _i, _p, _p, _p, _p], _i),
     "wush_transform_quant": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _p], _i),
     "wush_transform_apply": ([_i, _i, _i, _i, _p, _p, _p, _p], _i),
+    "wush_build_shared": ([_i, _i, _i, _i, _p, _p, _i, _p, _p, _p], _i),
+    "wush_transform_quant_shared": ([_i, _i, _i, _i, _p, _p, _i, _p, _f, _p, _p, _p], _i),
+    "wush_nvfp4_global_scale_shared": ([_i, _i, _i, _p, _p, _i, _p, _p, _p], _i),
+    "wush_pack_weights_shared": ([_i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p], _i),
     "wush_nvfp4_global_scale": ([_i, _i, _i, _p, _p, _fp, _p], _i),
     "wush_pack_weights": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
     "wush_build_hd": ([_i, _i, _i, _p, _p, _p, _p], _i),
@@ -150,6 +154,53 @@ def wush_transform_apply(X, Tx, Y, stream=None):
     xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
     _check(lib.wush_transform_apply(xdt, Tx.shape[-1], n, d_in, _ptr(X), _ptr(Tx), _ptr(Y), _stream(stream)),
            "wush_transform_apply")
+
+
+def wush_build_shared(kind, W, Sx, bs, group, ngroups):
+    """Host numpy: per-group (Tx, Tw) [ngroups][bs][bs] float32 from the groups' summed moments."""
+    import numpy as np
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    d_out, d_in = W.shape
+    group = np.ascontiguousarray(group, dtype=np.int32)
+    Sx = None if Sx is None else np.ascontiguousarray(Sx, dtype=np.float32)
+    Tx = np.empty((ngroups, bs, bs), dtype=np.float32)
+    Tw = np.empty_like(Tx)
+    _check(lib.wush_build_shared(KINDS[kind], bs, d_in, d_out, W.ctypes.data,
+                                 None if Sx is None else Sx.ctypes.data, int(ngroups), group.ctypes.data,
+                                 Tx.ctypes.data, Tw.ctypes.data), "wush_build_shared")
+    return Tx, Tw
+
+
+def wush_transform_quant_shared(fmt, X, Tx, group, codes, scales, g=0.0, stream=None):
+    """X: device [n][d_in] f32/bf16; Tx: device [ngroups][bs][bs] f32; group: device [nblk] int32."""
+    import torch
+    n, d_in = X.shape
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("X must be float32 or bfloat16")
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    _check(lib.wush_transform_quant_shared(_fmt(fmt), xdt, n, d_in, _ptr(X), _ptr(Tx), Tx.shape[0], _ptr(group),
+                                           float(g), _ptr(codes), _ptr(scales), _stream(stream)),
+           "wush_transform_quant_shared")
+
+
+def wush_nvfp4_global_scale_shared(X, Tx, group, stream=None):
+    import torch
+    n, d_in = X.shape
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    g = ctypes.c_float(0.0)
+    _check(lib.wush_nvfp4_global_scale_shared(xdt, n, d_in, _ptr(X), _ptr(Tx), Tx.shape[0], _ptr(group),
+                                              ctypes.byref(g), _stream(stream)), "wush_nvfp4_global_scale_shared")
+    return g.value
+
+
+def wush_pack_weights_shared(fmt, W, Tw, group, codes, scales, stream=None):
+    """W: device [d_out][d_in] f32.  Returns the NVFP4 tensor scale (1.0 for other formats)."""
+    d_out, d_in = W.shape
+    g = ctypes.c_float(0.0)
+    _check(lib.wush_pack_weights_shared(_fmt(fmt), d_out, d_in, _ptr(W), _ptr(Tw), Tw.shape[0], _ptr(group),
+                                        _ptr(codes), _ptr(scales), ctypes.byref(g), _stream(stream)),
+           "wush_pack_weights_shared")
+    return g.value
 
 
 def wush_nvfp4_global_scale(X, Tx, stream=None):

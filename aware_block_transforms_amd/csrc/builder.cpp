@@ -338,6 +338,68 @@ wush_status wush_build_transforms(wush_kind kind, int bs, int d_in, int d_out, c
 // From the moment diagonals a_i = sum_o W[o][i]^2 and b_i = Sx_b[i][i]:
 // d_x = sqrt(sqrt(a / b)) / sqrt(bs), d_w = sqrt(sqrt(b / a)) / sqrt(bs),
 // the optimum of the proxy among Hadamard-times-diagonal transforms.
+wush_status wush_build_shared(wush_kind kind, int bs, int d_in, int d_out, const float* W, const float* Sx,
+                              int ngroups, const int* group, float* Tx, float* Tw) {
+  WUSH_REQUIRE(Tx && Tw && group, WUSH_E_ARG, "wush_build_shared: null pointer");
+  WUSH_REQUIRE(kind >= WUSH_IDENTITY && kind <= WUSH_WUSH, WUSH_E_ARG, "wush_build_shared: bad kind %d",
+               static_cast<int>(kind));
+  WUSH_REQUIRE(bs == 16 || bs == 32, WUSH_E_SHAPE, "wush_build_shared: bs must be 16 or 32 (got %d)", bs);
+  WUSH_REQUIRE(d_in >= bs && d_in % bs == 0, WUSH_E_SHAPE, "wush_build_shared: d_in %% bs != 0 (d_in=%d)", d_in);
+  const int nblk = d_in / bs;
+  WUSH_REQUIRE(ngroups >= 1 && ngroups <= nblk, WUSH_E_ARG, "wush_build_shared: need 1 <= ngroups <= %d", nblk);
+  std::vector<int> count(ngroups, 0);
+  for (int b = 0; b < nblk; ++b) {
+    WUSH_REQUIRE(group[b] >= 0 && group[b] < ngroups, WUSH_E_ARG, "wush_build_shared: block %d has group %d", b,
+                 group[b]);
+    ++count[group[b]];
+  }
+  for (int gi = 0; gi < ngroups; ++gi)
+    WUSH_REQUIRE(count[gi] > 0, WUSH_E_ARG, "wush_build_shared: group %d owns no block", gi);
+  const size_t msz = static_cast<size_t>(bs) * bs;
+  if (kind == WUSH_IDENTITY || kind == WUSH_HADAMARD)   // data-free: every group gets the same matrix
+    return wush_build_transforms(kind, bs, ngroups * bs, d_out, nullptr, nullptr, Tx, Tw);
+  WUSH_REQUIRE(W && Sx, WUSH_E_ARG, "wush_build_shared: W and Sx are required for WUS/WUSH");
+  WUSH_REQUIRE(d_out >= 1, WUSH_E_SHAPE, "wush_build_shared: d_out must be >= 1");
+  // per-block weight moments (fp64), then the sums over each group's blocks in block order
+  std::vector<double> Ab(static_cast<size_t>(nblk) * msz, 0.0);
+  wush::parallel_blocks(nblk, [&](int b) {
+    double* A = Ab.data() + static_cast<size_t>(b) * msz;
+    for (int o = 0; o < d_out; ++o) {
+      const float* w = W + static_cast<size_t>(o) * d_in + static_cast<size_t>(b) * bs;
+      for (int i = 0; i < bs; ++i) {
+        const double wi = w[i];
+        for (int j = 0; j <= i; ++j) A[i * bs + j] += wi * static_cast<double>(w[j]);
+      }
+    }
+    for (int i = 0; i < bs; ++i)
+      for (int j = 0; j < i; ++j) A[j * bs + i] = A[i * bs + j];
+  });
+  std::atomic<int> bad_group{-1};
+  wush::parallel_blocks(ngroups, [&](int gi) {
+    std::vector<double> A(msz, 0.0), B(msz, 0.0), tx(msz), tw(msz);
+    for (int b = 0; b < nblk; ++b) {
+      if (group[b] != gi) continue;
+      const double* a = Ab.data() + static_cast<size_t>(b) * msz;
+      for (size_t i = 0; i < msz; ++i) {
+        A[i] += a[i];
+        B[i] += Sx[static_cast<size_t>(b) * msz + i];
+      }
+    }
+    if (!wush::block_transform(kind == WUSH_WUSH, bs, A.data(), B.data(), tx.data(), tw.data())) {
+      bad_group = gi;
+      return;
+    }
+    for (size_t i = 0; i < msz; ++i) {
+      Tx[gi * msz + i] = static_cast<float>(tx[i]);
+      Tw[gi * msz + i] = static_cast<float>(tw[i]);
+    }
+  });
+  if (bad_group.load() >= 0)
+    return fail(WUSH_E_NUMERIC, "wush_build_shared: group %d weight moment not positive definite after damping",
+                bad_group.load());
+  return WUSH_OK;
+}
+
 wush_status wush_build_hd(int bs, int d_in, int d_out, const float* W, const float* Sx, float* dx, float* dw) {
   WUSH_REQUIRE(W && Sx && dx && dw, WUSH_E_ARG, "wush_build_hd: null pointer");
   WUSH_REQUIRE(bs == 16 || bs == 32, WUSH_E_SHAPE, "wush_build_hd: bs must be 16 or 32 (got %d)", bs);

@@ -260,13 +260,16 @@ __device__ __forceinline__ void encode_store(const float (&y)[BS], size_t row, i
 template <int BS, int FMT, bool BF16, bool IDENT>
 __global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves_per_eu(4))) void tq_kernel(
     const void* __restrict__ X, const float* __restrict__ T, int n, int d_in, float g,
-    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out) {
+    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out,
+    const int* __restrict__ tmap, int ngroups) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = d_in / BS;
   const int blk = blockIdx.x * kWavesPerGroup + wave;
   if (blk >= nblk) return;                       // wave-uniform
   const float* __restrict__ Tb = IDENT ? nullptr : T + static_cast<size_t>(blk) * BS * BS;
+  (void)tmap;
+  (void)ngroups;
   const int tok0 = blockIdx.y * (2 * kWave) + lane, tok1 = tok0 + kWave;
   const bool v0 = tok0 < n, v1 = tok1 < n;
   uint32_t run_max = 0;
@@ -498,7 +501,8 @@ template <int BS, int FMT, bool BF16>
 // restrict-qualified loads freely and would issue x's before T's.)
 __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_mfma_kernel(
     const void* X, const float* T, int n, int d_in, float g,
-    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out) {
+    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out,
+    const int* __restrict__ tmap, int ngroups) {
   using U = XUnit<BS, BF16>;
   constexpr int H = BS / 16, C = BS / 4, D = kMfmaDepth;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kWavesPerGroup * U::kLdsDwords];
@@ -515,7 +519,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_mfma_kernel(
   const size_t col = static_cast<size_t>(blk) * BS;
   const int t0 = blockIdx.y * (kMfmaUnits * U::kRows);
   uint32_t run_max = 0;
-  const uint4* tp = reinterpret_cast<const uint4*>(T + static_cast<size_t>(blk) * BS * BS);
+  // the block's matrix, or with a group map its group's (ids clamped to the table)
+  const int tsel = tmap ? min(max(tmap[blk], 0), ngroups - 1) : blk;
+  const uint4* tp = reinterpret_cast<const uint4*>(T + static_cast<size_t>(tsel) * BS * BS);
   constexpr int NT = BS * BS / 256;   // pieces of T per lane (4 or 1)
   const uint4 tv0 = tp[lane];
   const uint4 tv1 = NT > 1 ? tp[lane + 64] : tv0;
@@ -592,7 +598,8 @@ __device__ __forceinline__ void hd_rotate(float (&v)[BS]) {
 template <int BS, int FMT, bool BF16>
 __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_hd_kernel(
     const void* __restrict__ X, const float* __restrict__ d, int n, int d_in, float g,
-    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out) {
+    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out,
+    const int* __restrict__ tmap, int ngroups) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = d_in / BS;
@@ -635,7 +642,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_hd_kernel(
 
 __global__ void fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
-using KernelFn = void (*)(const void*, const float*, int, int, float, uint8_t*, void*, uint32_t*);
+using KernelFn = void (*)(const void*, const float*, int, int, float, uint8_t*, void*, uint32_t*, const int*, int);
 
 template <int BS, int FMT>
 KernelFn pick(bool bf16, bool ident) {
@@ -666,7 +673,8 @@ KernelFn select_kernel(int fmt, int bs, bool bf16, bool ident) {
 }
 
 wush_status launch(int fmt, int bs, bool bf16, int n, int d_in, const void* X, const float* T, float g,
-                   uint8_t* codes, void* scales, uint32_t* amax, hipStream_t stream) {
+                   uint8_t* codes, void* scales, uint32_t* amax, hipStream_t stream, const int* tmap = nullptr,
+                   int ngroups = 0) {
   if (n == 0) return WUSH_OK;
   if (!wush::aligned16(T)) return wush::fail(WUSH_E_ARG, "transform_quant: T must be 16-byte aligned");
   KernelFn k = select_kernel(fmt, bs, bf16, T == nullptr);
@@ -677,7 +685,8 @@ wush_status launch(int fmt, int bs, bool bf16, int n, int d_in, const void* X, c
                                                 : (bf16 ? XUnit<16, true>::kRows : XUnit<16, false>::kRows));
   dim3 grid((nblk + kWavesPerGroup - 1) / kWavesPerGroup, (n + per_wave - 1) / per_wave);
   if (grid.y > 65535u) return wush::fail(WUSH_E_SHAPE, "transform_quant: n=%d too large", n);
-  hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, T, n, d_in, g, codes, scales, amax);
+  hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, T, n, d_in, g, codes, scales, amax, tmap,
+                     ngroups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "transform_quant launch: %s", hipGetErrorString(e));
   return WUSH_OK;
@@ -708,7 +717,8 @@ wush_status launch_hd(int fmt, int bs, bool bf16, int n, int d_in, const void* X
   const int per_group = kWavesPerGroup * kHdTokens;
   dim3 grid((nblk + kWave - 1) / kWave, (n + per_group - 1) / per_group);
   if (grid.y > 65535u) return wush::fail(WUSH_E_SHAPE, "transform_quant_hd: n=%d too large", n);
-  hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, d, n, d_in, g, codes, scales, amax);
+  hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, d, n, d_in, g, codes, scales, amax,
+                     static_cast<const int*>(nullptr), 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "transform_quant_hd launch: %s", hipGetErrorString(e));
   return WUSH_OK;
@@ -717,17 +727,17 @@ wush_status launch_hd(int fmt, int bs, bool bf16, int n, int d_in, const void* X
 // max|T x| over a tensor, written to a device uint (float bits).
 // (T is a dense [nblk][bs][bs] matrix, or with hd the per-channel scales.)
 wush_status tensor_amax(int bs, bool bf16, int n, int d_in, const void* X, const float* T, bool hd,
-                        uint32_t* amax_dev, hipStream_t stream) {
+                        uint32_t* amax_dev, hipStream_t stream, const int* tmap, int ngroups) {
   hipLaunchKernelGGL(fill_u32, dim3(1), dim3(1), 0, stream, amax_dev, 0u);
   if (hd) return launch_hd(kAmax, bs, bf16, n, d_in, X, T, 0.0f, nullptr, nullptr, amax_dev, stream);
-  return launch(kAmax, bs, bf16, n, d_in, X, T, 0.0f, nullptr, nullptr, amax_dev, stream);
+  return launch(kAmax, bs, bf16, n, d_in, X, T, 0.0f, nullptr, nullptr, amax_dev, stream, tmap, ngroups);
 }
 
 wush_status global_scale(int bs, bool bf16, int n, int d_in, const void* X, const float* T, bool hd, float* g_out,
-                         hipStream_t stream) {
+                         hipStream_t stream, const int* tmap = nullptr, int ngroups = 0) {
   uint32_t* dbuf = nullptr;
   if (hipMalloc(&dbuf, sizeof(uint32_t)) != hipSuccess) return wush::fail(WUSH_E_HIP, "global_scale: hipMalloc failed");
-  wush_status st = tensor_amax(bs, bf16, n, d_in, X, T, hd, dbuf, stream);
+  wush_status st = tensor_amax(bs, bf16, n, d_in, X, T, hd, dbuf, stream, tmap, ngroups);
   uint32_t bits = 0;
   if (st == WUSH_OK) {
     if (hipMemcpyAsync(&bits, dbuf, sizeof bits, hipMemcpyDeviceToHost, stream) != hipSuccess ||
@@ -859,6 +869,56 @@ wush_status wush_pack_weights_hd(wush_format fmt, int d_out, int d_in, const flo
   }
   const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
   return launch_hd(fk, wush_format_block(fmt), false, d_out, d_in, W, dw, g, codes, scales, nullptr, s);
+}
+
+wush_status wush_transform_quant_shared(wush_format fmt, wush_dtype xdt, int n, int d_in, const void* X,
+                                        const float* Tx, int ngroups, const int* group, float g, uint8_t* codes,
+                                        void* scales, void* stream) {
+  wush_status st = check_common("wush_transform_quant_shared", fmt, n, d_in, X, codes, scales);
+  if (st != WUSH_OK) return st;
+  if (xdt != WUSH_F32 && xdt != WUSH_BF16) return wush::fail(WUSH_E_ARG, "wush_transform_quant_shared: bad dtype");
+  if (ngroups < 1) return wush::fail(WUSH_E_ARG, "wush_transform_quant_shared: ngroups must be >= 1");
+  if (n > 0 && (!Tx || !group)) return wush::fail(WUSH_E_ARG, "wush_transform_quant_shared: null Tx or group map");
+  if (fmt == WUSH_NVFP4 && !(g > 0.0f && g < 3.0e38f))
+    return wush::fail(WUSH_E_ARG, "wush_transform_quant_shared: NVFP4 needs a positive finite tensor scale g");
+  const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
+  return launch(fk, wush_format_block(fmt), xdt == WUSH_BF16, n, d_in, X, Tx, g, codes, scales, nullptr,
+                static_cast<hipStream_t>(stream), group, ngroups);
+}
+
+wush_status wush_nvfp4_global_scale_shared(wush_dtype xdt, int n, int d_in, const void* X, const float* Tx,
+                                           int ngroups, const int* group, float* g_out, void* stream) {
+  if (!X || !Tx || !group || !g_out) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale_shared: null pointer");
+  if (xdt != WUSH_F32 && xdt != WUSH_BF16)
+    return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale_shared: bad dtype");
+  if (ngroups < 1) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale_shared: ngroups must be >= 1");
+  if (n < 1 || d_in < 16 || d_in % 16 != 0)
+    return wush::fail(WUSH_E_SHAPE, "wush_nvfp4_global_scale_shared: need n >= 1 and d_in %% 16 == 0");
+  if (!wush::aligned16(X)) return wush::fail(WUSH_E_ARG, "wush_nvfp4_global_scale_shared: X must be 16-byte aligned");
+  return global_scale(16, xdt == WUSH_BF16, n, d_in, X, Tx, false, g_out, static_cast<hipStream_t>(stream), group,
+                      ngroups);
+}
+
+wush_status wush_pack_weights_shared(wush_format fmt, int d_out, int d_in, const float* W, const float* Tw,
+                                     int ngroups, const int* group, uint8_t* codes, void* scales, float* g_out,
+                                     void* stream) {
+  wush_status st = check_common("wush_pack_weights_shared", fmt, d_out, d_in, W, codes, scales);
+  if (st != WUSH_OK) return st;
+  if (ngroups < 1) return wush::fail(WUSH_E_ARG, "wush_pack_weights_shared: ngroups must be >= 1");
+  if (d_out > 0 && (!Tw || !group)) return wush::fail(WUSH_E_ARG, "wush_pack_weights_shared: null Tw or group map");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float g = 0.0f;
+  if (fmt == WUSH_NVFP4) {
+    if (!g_out) return wush::fail(WUSH_E_ARG, "wush_pack_weights_shared: NVFP4 needs g_out");
+    if (d_out < 1) return wush::fail(WUSH_E_SHAPE, "wush_pack_weights_shared: NVFP4 needs d_out >= 1");
+    st = global_scale(16, false, d_out, d_in, W, Tw, false, &g, s, group, ngroups);
+    if (st != WUSH_OK) return st;
+    *g_out = g;
+  } else if (g_out) {
+    *g_out = 1.0f;
+  }
+  const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
+  return launch(fk, wush_format_block(fmt), false, d_out, d_in, W, Tw, g, codes, scales, nullptr, s, group, ngroups);
 }
 
 }  // extern "C"

@@ -59,6 +59,8 @@ def parse():
                     help="identity | hadamard | wus | wush, or hd (the Hadamard-diagonal variant)")
     ap.add_argument("--batch", type=int, default=1, help="had256: batch 1..16")
     ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--shared", type=int, default=0, metavar="G",
+                    help="wus/wush: share one matrix per group of nblk/G adjacent blocks (shared-transform variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
@@ -72,7 +74,7 @@ def parse():
 class Layer:
     """One quantized linear layer, device resident, with `rotate` copies of its inputs."""
 
-    def __init__(self, wl, fmt, kind, rotate, W, torch):
+    def __init__(self, wl, fmt, kind, rotate, W, torch, shared=0):
         from synth.gen import make_weights, make_activations, bf16_bits
         self.wl, self.fmt, self.kind = wl, fmt, kind
         self.bs = W.BLOCK[fmt]
@@ -85,6 +87,9 @@ class Layer:
         Sx = np.empty((nblk, self.bs, self.bs), np.float32)
         W.wush_block_moments(self.bs, X, Sx)
         self.hd = kind == "hd"
+        # shared-transform variant: G groups of adjacent blocks
+        self.group = (np.arange(nblk) * shared // nblk).astype(np.int32) if shared and kind in ("wus", "wush") else None
+        self.ngroups = shared
         dev = "cuda"
         sdt = torch.int16 if fmt == "int4" else torch.uint8
         Wd = torch.from_numpy(Wt).to(dev)
@@ -102,6 +107,12 @@ class Layer:
             self.Tx = torch.from_numpy(Tx).to(dev)
             self.w_g = W.wush_pack_weights_hd(fmt, Wd, torch.from_numpy(Tw).to(dev), wc, wsc)
             self.x_g = W.wush_nvfp4_global_scale_hd(xd, self.Tx) if fmt == "nvfp4" else 1.0
+        elif self.group is not None:
+            Tx, Tw = W.wush_build_shared(kind, Wt, Sx, self.bs, self.group, shared)
+            self.Tx = torch.from_numpy(Tx).to(dev)
+            self.gdev = torch.from_numpy(self.group).to(dev)
+            self.w_g = W.wush_pack_weights_shared(fmt, Wd, torch.from_numpy(Tw).to(dev), self.gdev, wc, wsc)
+            self.x_g = W.wush_nvfp4_global_scale_shared(xd, self.Tx, self.gdev) if fmt == "nvfp4" else 1.0
         else:
             Tx = np.empty_like(Sx)
             Tw = np.empty_like(Sx)
@@ -159,6 +170,8 @@ def run_layer_steps(layers, W, torch, steps, warmup, rotate):
                 ev[li][0].record(stream)
             if L.hd:
                 W.wush_transform_quant_hd(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
+            elif L.group is not None:
+                W.wush_transform_quant_shared(L.fmt, L.X[r], L.Tx, L.gdev, L.xc, L.xsc, g=L.x_g)
             else:
                 W.wush_transform_quant(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
             if ev is not None:
@@ -245,6 +258,12 @@ def cpu_baseline(L, target_s):
 
         def tq(T, rows, gg):
             return quant.transform_quant_hd(L.fmt, T, rows, g=gg)
+    elif L.group is not None:
+        Tg, Twg, _, _ = transforms.build_shared(L.kind, Wt, Sx, L.bs, L.group, L.ngroups)
+        Tx, Tw = transforms.expand_shared(Tg, L.group), transforms.expand_shared(Twg, L.group)
+
+        def tq(T, rows, gg):
+            return quant.transform_quant(L.fmt, T, rows, g=gg)
     else:
         Tx, Tw, _, _ = transforms.build_transforms(L.kind, Wt, Sx, L.bs)
 
@@ -330,7 +349,7 @@ def main():
         wls = [CONFIGS[args.workload]]
     fmt = args.fmt or wls[0].formats[0]
     kind = args.kind or ("wush" if "wush" in wls[0].kinds else wls[0].kinds[-1])
-    layers = [Layer(wl, fmt, kind, args.rotate, W, torch) for wl in wls]
+    layers = [Layer(wl, fmt, kind, args.rotate, W, torch, shared=args.shared) for wl in wls]
 
     ms_step, tq_ms, gm_ms = run_layer_steps(layers, W, torch, args.steps, args.warmup, args.rotate)
 
@@ -358,7 +377,8 @@ def main():
         roof_gemm.update({"bound": "alu", "achieved": round(rescale, 2), "peak": round(VALU_TOPS, 1),
                           "unit": "Top/s", "frac": round(rescale / VALU_TOPS, 4),
                           "int8_TOPS": round(gemm_achieved, 2), "int8_frac": round(gemm_achieved / INT8_TOPS, 4)})
-    tq_name = "wush_transform_quant_hd" if layers[0].hd else "wush_transform_quant"
+    tq_name = ("wush_transform_quant_hd" if layers[0].hd else
+               "wush_transform_quant_shared" if layers[0].group is not None else "wush_transform_quant")
     # dense transforms: fp32 matrix cores; the diagonal variant: vector ALU
     tq_peak, tq_bound = (VALU_FP32_TFLOPS, "alu") if layers[0].hd else (MFMA_FP32_TFLOPS, "mfma")
     t_alu = tq_flops / (tq_peak * 1e12)
@@ -389,7 +409,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wname, "transform": kind, "format": fmt,
                    "x_dtype": x_dtype, "tokens": layers[0].M,
-                   "layers": [[L.K, L.N] for L in layers], "rotate_buffers": args.rotate},
+                   "layers": [[L.K, L.N] for L in layers], "rotate_buffers": args.rotate,
+                   **({"shared_groups": args.shared} if layers[0].group is not None else {})},
         "quant_GBps": round(tq_gbps, 1),
         "tq_us": round(tq_t * 1e6, 2),
         "gemm_us": round(gm_t * 1e6, 2),

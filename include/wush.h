@@ -117,6 +117,20 @@ wush_status wush_block_moments_dev(int bs, wush_dtype xdt, int n, int d_in, cons
 wush_status wush_build_transforms(wush_kind kind, int bs, int d_in, int d_out,
                                   const float* W, const float* Sx, float* Tx, float* Tw);
 
+/* Shared-transform variant ([WUSH-news], paragraph on deployment limits:
+ * similar blocks share one transform).  The caller assigns each block b a
+ * group group[b] in [0, ngroups); every group must own a block.  A group's
+ * matrices are those of wush_build_transforms for the group's summed moments
+ *   A_G = sum_{b in G} W_b W_b^T,  B_G = sum_{b in G} Sx_b   (fp64, block order),
+ * (a reading: the pages give no construction for the shared matrix).
+ *   group   host, [d_in/bs] int32.
+ *   Tx, Tw  host out, [ngroups][bs][bs] fp32.
+ * Errors: those of wush_build_transforms; WUSH_E_ARG for a group id out of
+ * range or an empty group. */
+wush_status wush_build_shared(wush_kind kind, int bs, int d_in, int d_out, const float* W,
+                              const float* Sx, int ngroups, const int* group, float* Tx,
+                              float* Tw);
+
 /* Hadamard-diagonal variant ([WUSH-news], deployment and limitation
  * paragraphs: the data-aware component approximated by a diagonal matrix).
  * Reading: the construction above with the moments replaced by their
@@ -193,6 +207,23 @@ wush_status wush_nvfp4_global_scale(wush_dtype xdt, int n, int d_in, const void*
 wush_status wush_pack_weights(wush_format fmt, int d_out, int d_in, const float* W,
                               const float* Tw, uint8_t* codes, void* scales,
                               float* g_out, void* stream);
+
+/* The shared-transform variant of the three calls above (matrices from
+ * wush_build_shared): block b of every row is transformed with group[b]'s
+ * matrix, with the same pinned arithmetic, quantizers, outputs and errors.
+ *   Tx / Tw  device, [ngroups][bs][bs] fp32, 16-byte aligned (not NULL).
+ *   group    device, [d_in/bs] int32; ids outside [0, ngroups) are clamped to
+ *            that range (no out-of-bounds read), so pass valid ids. */
+wush_status wush_transform_quant_shared(wush_format fmt, wush_dtype xdt, int n, int d_in,
+                                        const void* X, const float* Tx, int ngroups,
+                                        const int* group, float g, uint8_t* codes,
+                                        void* scales, void* stream);
+wush_status wush_nvfp4_global_scale_shared(wush_dtype xdt, int n, int d_in, const void* X,
+                                           const float* Tx, int ngroups, const int* group,
+                                           float* g_out, void* stream);
+wush_status wush_pack_weights_shared(wush_format fmt, int d_out, int d_in, const float* W,
+                                     const float* Tw, int ngroups, const int* group,
+                                     uint8_t* codes, void* scales, float* g_out, void* stream);
 
 /* The Hadamard-diagonal variant of the three calls above (scales from
  * wush_build_hd, device pointers, [d_in] fp32).  The transform per token (or

@@ -223,6 +223,35 @@ def test_build_hd_matches_oracle_and_rejects_bad_input():
     assert L.wush_nvfp4_global_scale_hd(0, 4, 128, None, None, None, None) == W.WUSH_E_ARG
 
 
+def test_build_shared_matches_oracle_and_rejects_bad_groups():
+    W_, X = random_case(46, 200, 256, 48)
+    for bs, group, ng in ((32, np.array([0, 1, 0, 2, 2, 1, 0, 1]), 3), (16, np.arange(16) % 5, 5),
+                          (32, np.zeros(8, dtype=np.int32), 1)):
+        Sx = tr.activation_moments(X, bs).astype(np.float32)
+        for kind in ("wus", "wush", "hadamard"):
+            Tx, Tw = W.wush_build_shared(kind, W_, Sx, bs, group, ng)
+            _, _, rx, rw = tr.build_shared(kind, W_, Sx, bs, group, ng)
+            # fp64 on both sides, summed in different orders, rounded to fp32:
+            # within 8 fp32 ulps of each group matrix's largest entry
+            for T, R in ((Tx, rx), (Tw, rw)):
+                tol = 8 * 2.0 ** -24 * np.abs(R).reshape(ng, -1).max(axis=1)[:, None, None]
+                assert np.all(np.abs(T - R) <= tol), (bs, kind)
+    L = W.lib
+    g = np.array([0, 1, 0, 3], dtype=np.int32)        # group 2 owns no block, 3 is out of range
+    buf = np.zeros(8192, np.float32)
+    p = buf.ctypes.data
+    assert L.wush_build_shared(3, 32, 128, 4, p, p, 3, g.ctypes.data, p, p) == W.WUSH_E_ARG
+    g = np.array([0, 1, 0, 0], dtype=np.int32)        # group 2 empty
+    assert L.wush_build_shared(3, 32, 128, 4, p, p, 3, g.ctypes.data, p, p) == W.WUSH_E_ARG
+    assert b"owns no block" in L.wush_last_error()
+    assert L.wush_build_shared(3, 32, 128, 4, p, p, 5, g.ctypes.data, p, p) == W.WUSH_E_ARG
+    assert L.wush_build_shared(3, 24, 128, 4, p, p, 1, g.ctypes.data, p, p) == W.WUSH_E_SHAPE
+    assert L.wush_transform_quant_shared(0, 0, 4, 128, None, None, 1, None, 0.0, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_transform_quant_shared(0, 0, 4, 100, None, None, 1, None, 0.0, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_pack_weights_shared(0, 4, 128, None, None, 1, None, None, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_nvfp4_global_scale_shared(0, 4, 128, None, None, 1, None, None, None) == W.WUSH_E_ARG
+
+
 def test_block_moments_dev_checks_and_workspace_size():
     L = W.lib
     # 300 tokens: 2 chunks of up to 256; 5000: 20; 20000: capped at 64

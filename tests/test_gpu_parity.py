@@ -106,6 +106,47 @@ def test_transform_apply_adversarial(bs, dtype):
     assert np.array_equal(host(Y).view(np.uint32), ref.view(np.uint32)), np.argwhere(host(Y) != ref)[:8]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_transform_quant_and_pack_shared_bit_exact(fmt, dtype):
+    # shared-transform variant: block b uses its group's matrix; the oracle
+    # expands the groups to per-block matrices and runs its own chain
+    bs = W.BLOCK[fmt]
+    for si, (n, d_in) in enumerate(SHAPES16 if bs == 16 else SHAPES32):
+        Wt, X = random_case(500 + si, n, d_in, 40, dtype=dtype)
+        nblk = d_in // bs
+        ng = min(3, nblk)
+        group = (np.arange(nblk) * 7 + si) % ng
+        group[:ng] = np.arange(ng)                     # every group owns a block
+        Sx = tr.activation_moments(X, bs).astype(np.float32)
+        Tg, Twg, _, _ = tr.build_shared("wush", Wt, Sx, bs, group, ng)
+        Tx, Tw = tr.expand_shared(Tg, group), tr.expand_shared(Twg, group)
+        gdev = to_dev(group.astype(np.int32))
+        g = None
+        if fmt == "nvfp4":
+            g = quant.nvfp4_tensor_scale(quant.apply_transform(Tx, X))
+            g_dev = W.wush_nvfp4_global_scale_shared(x_dev(X, dtype), to_dev(Tg), gdev)
+            assert np.float32(g_dev) == g
+        rc, rs = quant.transform_quant(fmt, Tx, X, g=g)
+        sdt = torch.int16 if fmt == "int4" else torch.uint8
+        codes = torch.empty((n, d_in // 2), dtype=torch.uint8, device=DEV)
+        sc = torch.empty((n, nblk), dtype=sdt, device=DEV)
+        W.wush_transform_quant_shared(fmt, x_dev(X, dtype), to_dev(Tg), gdev, codes, sc, g=g or 0.0)
+        torch.cuda.synchronize()
+        assert np.array_equal(scales_np(sc, fmt), rs), (fmt, dtype, n, d_in)
+        assert np.array_equal(host(codes), rc), (fmt, dtype, n, d_in)
+        # weights
+        gw = quant.nvfp4_tensor_scale(quant.apply_transform(Tw, Wt)) if fmt == "nvfp4" else None
+        wc, ws_ = quant.transform_quant(fmt, Tw, Wt, g=gw)
+        codes = torch.empty((Wt.shape[0], d_in // 2), dtype=torch.uint8, device=DEV)
+        sc = torch.empty((Wt.shape[0], nblk), dtype=sdt, device=DEV)
+        g_w = W.wush_pack_weights_shared(fmt, to_dev(Wt), to_dev(Twg), gdev, codes, sc)
+        torch.cuda.synchronize()
+        if fmt == "nvfp4":
+            assert np.float32(g_w) == gw
+        assert np.array_equal(scales_np(sc, fmt), ws_) and np.array_equal(host(codes), wc), (fmt, n, d_in)
+
+
 def _edge_inputs(d_in):
     rng = np.random.default_rng(77)
     X = rng.standard_normal((9, d_in)).astype(np.float32)
