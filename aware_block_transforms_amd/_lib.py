@@ -44,6 +44,10 @@ _SIGS = {
     "wush_transform_quant": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _p], _i),
     "wush_transform_apply": ([_i, _i, _i, _i, _p, _p, _p, _p], _i),
     "wush_build_shared": ([_i, _i, _i, _i, _p, _p, _i, _p, _p, _p], _i),
+    "wush_mxfp4_planes_bytes": ([_i, _i], _sz),
+    "wush_mxfp4_scale_planes": ([_i, _i, _p, _p, _p], _i),
+    "wush_transform_quant_mx_planes": ([_i, _i, _i, _p, _p, _p, _p, _p], _i),
+    "wush_w4a4_gemm_mx_planes": ([_i, _i, _i, _p, _p, _p, _p, _p, _p], _i),
     "wush_transform_quant_shared": ([_i, _i, _i, _i, _p, _p, _i, _p, _f, _p, _p, _p], _i),
     "wush_nvfp4_global_scale_shared": ([_i, _i, _i, _p, _p, _i, _p, _p, _p], _i),
     "wush_pack_weights_shared": ([_i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p], _i),
@@ -201,6 +205,33 @@ def wush_pack_weights_shared(fmt, W, Tw, group, codes, scales, stream=None):
                                         _ptr(codes), _ptr(scales), ctypes.byref(g), _stream(stream)),
            "wush_pack_weights_shared")
     return g.value
+
+
+def wush_mxfp4_planes_bytes(rows, K):
+    return lib.wush_mxfp4_planes_bytes(rows, K)
+
+
+def wush_mxfp4_scale_planes(scales, planes, K, stream=None):
+    """scales: device [rows][K/32] uint8 (row-major) -> planes: device uint8 of wush_mxfp4_planes_bytes."""
+    _check(lib.wush_mxfp4_scale_planes(scales.shape[0], K, _ptr(scales), _ptr(planes), _stream(stream)),
+           "wush_mxfp4_scale_planes")
+
+
+def wush_transform_quant_mx_planes(X, Tx, codes, planes, stream=None):
+    import torch
+    n, d_in = X.shape
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("X must be float32 or bfloat16")
+    xdt = DTYPES["bf16"] if X.dtype == torch.bfloat16 else DTYPES["f32"]
+    _check(lib.wush_transform_quant_mx_planes(xdt, n, d_in, _ptr(X), _ptr(Tx), _ptr(codes), _ptr(planes),
+                                              _stream(stream)), "wush_transform_quant_mx_planes")
+
+
+def wush_w4a4_gemm_mx_planes(a_codes, a_planes, b_codes, b_planes, Y, stream=None):
+    M, N = Y.shape
+    K = a_codes.shape[1] * 2
+    _check(lib.wush_w4a4_gemm_mx_planes(M, N, K, _ptr(a_codes), _ptr(a_planes), _ptr(b_codes), _ptr(b_planes),
+                                        _ptr(Y), _stream(stream)), "wush_w4a4_gemm_mx_planes")
 
 
 def wush_nvfp4_global_scale(X, Tx, stream=None):

@@ -15,6 +15,9 @@ namespace wush {
 size_t gemm_mxfp4_ws_bytes(int M, int N, int K);
 wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
                        float* Y, void* ws, size_t ws_bytes, hipStream_t stream);
+wush_status mxfp4_scale_planes(int rows, int K, const uint8_t* S, uint8_t* P, hipStream_t stream);
+wush_status gemm_mxfp4_planes(int M, int N, int K, const uint8_t* A, const uint8_t* PA, const uint8_t* B,
+                              const uint8_t* PB, float* Y, hipStream_t stream);
 size_t gemm_nvfp4_ws_bytes(int M, int N, int K);
 wush_status gemm_nvfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, float ga, const uint8_t* B,
                        const uint8_t* SB, float gb, float* Y, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -58,4 +61,27 @@ extern "C" wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K, cons
                              static_cast<const uint16_t*>(b_scales), Y, ws, ws_bytes, s);
   }
   return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm: bad format");
+}
+
+extern "C" wush_status wush_mxfp4_scale_planes(int rows, int K, const uint8_t* scales, uint8_t* planes,
+                                               void* stream) {
+  if (rows < 1 || K < 256 || K % 256 != 0)
+    return wush::fail(WUSH_E_SHAPE, "wush_mxfp4_scale_planes: need rows >= 1 and K a multiple of 256");
+  if (!scales || !planes) return wush::fail(WUSH_E_ARG, "wush_mxfp4_scale_planes: null pointer");
+  if ((reinterpret_cast<uintptr_t>(scales) & 3u) || !wush::aligned16(planes))
+    return wush::fail(WUSH_E_ARG, "wush_mxfp4_scale_planes: scales 4-byte and planes 16-byte aligned");
+  return wush::mxfp4_scale_planes(rows, K, scales, planes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" wush_status wush_w4a4_gemm_mx_planes(int M, int N, int K, const uint8_t* a_codes, const uint8_t* a_planes,
+                                                const uint8_t* b_codes, const uint8_t* b_planes, float* Y,
+                                                void* stream) {
+  if (M < 1 || N < 1 || K < 256 || K % 256)
+    return wush::fail(WUSH_E_SHAPE, "wush_w4a4_gemm_mx_planes: need M, N >= 1 and K a multiple of 256");
+  if (!a_codes || !a_planes || !b_codes || !b_planes || !Y)
+    return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm_mx_planes: null pointer");
+  if (!wush::aligned16(a_codes) || !wush::aligned16(b_codes) || !wush::aligned16(Y) || !wush::aligned16(a_planes) ||
+      !wush::aligned16(b_planes))
+    return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm_mx_planes: codes, planes and Y must be 16-byte aligned");
+  return wush::gemm_mxfp4_planes(M, N, K, a_codes, a_planes, b_codes, b_planes, Y, static_cast<hipStream_t>(stream));
 }

@@ -552,6 +552,31 @@ size_t gemm_mxfp4_ws_bytes(int M, int N, int K) {
   return (tiles_m + tiles_n) * nb * kScaleOp;
 }
 
+// scales of one operand (rows x K/32 bytes, row-major) into plane order
+wush_status mxfp4_scale_planes(int rows, int K, const uint8_t* S, uint8_t* P, hipStream_t stream) {
+  const int tiles = (rows + kBM - 1) / kBM, nb = K / 256;
+  hipLaunchKernelGGL(scales_to_planes, dim3(tiles, (nb + 1) / 2), dim3(256), 0, stream, S, rows,
+                     static_cast<const uint8_t*>(nullptr), 0, tiles, K, nb, P);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_mxfp4_scale_planes launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
+// the LDS kernel on scales already in plane order (K a multiple of 256)
+wush_status gemm_mxfp4_planes(int M, int N, int K, const uint8_t* A, const uint8_t* PA, const uint8_t* B,
+                              const uint8_t* PB, float* Y, hipStream_t stream) {
+  if (!use_lds_kernel(M, N, K) || K % 256 != 0)
+    return fail(WUSH_E_UNSUPPORTED, "wush_w4a4_gemm_mx_planes: needs K a multiple of 256 and operands below 2 GiB");
+  const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+  const long tiles = static_cast<long>(tiles_m) * tiles_n;
+  if (tiles > 0x7fffffffL) return fail(WUSH_E_SHAPE, "wush_w4a4_gemm_mx_planes: too many tiles");
+  hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, PA, B, PB, Y, M, N,
+                     K);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm_mx_planes launch: %s", hipGetErrorString(e));
+  return WUSH_OK;
+}
+
 wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
                        float* Y, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (use_lds_kernel(M, N, K)) {

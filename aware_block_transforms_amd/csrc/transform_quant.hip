@@ -36,7 +36,9 @@ constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;
 constexpr int kTokensPerWave = 2 * kWave;   // two 64-token tiles per wave
 
-enum Fmt { kMX = 0, kNV = 1, kI4 = 2, kAmax = 3, kApply = 4 };   // kApply: write y itself (fp32)
+// kApply: write y itself (fp32); kMXP: MXFP4 with the scales written in the
+// plane order of the MXFP4 matmul's LDS stage (see mxfp4_plane_offset)
+enum Fmt { kMX = 0, kNV = 1, kI4 = 2, kAmax = 3, kApply = 4, kMXP = 5 };
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -231,6 +233,18 @@ __device__ __forceinline__ void store_scale(void* __restrict__ scales, size_t id
     reinterpret_cast<uint16_t*>(scales)[idx] = static_cast<uint16_t>(s);
   else
     reinterpret_cast<uint8_t*>(scales)[idx] = static_cast<uint8_t>(s);
+}
+
+// Byte offset of the E8M0 scale of (row, 32-wide group gi) in the plane order
+// the MXFP4 matmul stages through LDS (its scales_to_planes pre-pass writes the
+// same layout): 2 KB per (256-row tile t, 256-wide K block kb) at
+// (t nb + kb) * 2048, plane b = gi % 8 at 256 b, lane row rr = r % 16 at 16 rr,
+// tile position 8 (r / 128) + (r / 16) % 8, rotated by 8 bytes in odd planes
+// (r = row % 256; nb = K / 256).
+__device__ __forceinline__ size_t mxfp4_plane_offset(int row, int gi, int nb) {
+  const int t = row >> 8, r = row & 255, kb = gi >> 3, b = gi & 7;
+  const int pos = (8 * (r >> 7) + ((r >> 4) & 7)) ^ (8 * (b & 1));
+  return (static_cast<size_t>(t) * nb + kb) * 2048 + b * 256 + (r & 15) * 16 + pos;
 }
 
 // Codes and scale of one token's block y (the pinned encoders); `amax` pass
@@ -468,9 +482,10 @@ __device__ __forceinline__ void mfma_group(const float (&ta)[BS / 16][BS / 4], c
   if constexpr (FMT == kAmax) {
     run_max = max(run_max, ab);                // rows past n repeat row n - 1
   } else {
-    const BlockQuant<FMT> q = block_quant<FMT>(ab, g);
+    constexpr int QF = FMT == kMXP ? kMX : FMT;
+    const BlockQuant<QF> q = block_quant<QF>(ab, g);
     uint32_t w[1];
-    encode_pairs<FMT, 2 * H>(y, q, w);
+    encode_pairs<QF, 2 * H>(y, q, w);
     // Lane group g holds code bytes 2g, 2g+1 (outputs 4g .. 4g+3) in its low
     // half and, at bs 32, bytes 8+2g, 9+2g in its high half.  Groups 2m and
     // 2m+1 together form dword m of the row (low halves) and, at bs 32,
@@ -492,7 +507,10 @@ __device__ __forceinline__ void mfma_group(const float (&ta)[BS / 16][BS / 4], c
     const uint32_t word = bitsel(0u - static_cast<uint32_t>(gq == 0 || gq == 3), own, other);
     uint8_t* dst = codes + static_cast<size_t>(row) * (d_in / 2) + static_cast<size_t>(blk) * (BS / 2);
     reinterpret_cast<uint32_t*>(dst)[BS == 32 ? gq : (gq & 1)] = word;
-    store_scale<FMT>(scales, static_cast<size_t>(row) * nblk + blk, q.scale);
+    if constexpr (FMT == kMXP)
+      reinterpret_cast<uint8_t*>(scales)[mxfp4_plane_offset(row, blk, nblk / 8)] = static_cast<uint8_t>(q.scale);
+    else
+      store_scale<FMT>(scales, static_cast<size_t>(row) * nblk + blk, q.scale);
   }
 }
 
@@ -651,6 +669,8 @@ KernelFn pick(bool bf16, bool ident) {
 }
 
 KernelFn select_kernel(int fmt, int bs, bool bf16, bool ident) {
+  if (fmt == kMXP) return (bs == 32 && !ident) ? (bf16 ? tq_mfma_kernel<32, kMXP, true> : tq_mfma_kernel<32, kMXP, false>)
+                                              : nullptr;
   if (fmt == kApply) {
     if (ident) return nullptr;
     if (bs == 32) return bf16 ? tq_mfma_kernel<32, kApply, true> : tq_mfma_kernel<32, kApply, false>;
@@ -780,6 +800,22 @@ wush_status wush_transform_quant(wush_format fmt, wush_dtype xdt, int n, int d_i
     return wush::fail(WUSH_E_ARG, "wush_transform_quant: NVFP4 needs a positive finite tensor scale g");
   const int fk = fmt == WUSH_MXFP4 ? kMX : fmt == WUSH_NVFP4 ? kNV : kI4;
   return launch(fk, wush_format_block(fmt), xdt == WUSH_BF16, n, d_in, X, Tx, g, codes, scales, nullptr,
+                static_cast<hipStream_t>(stream));
+}
+
+size_t wush_mxfp4_planes_bytes(int rows, int K) {
+  if (rows < 1 || K < 256 || K % 256 != 0) return 0;
+  return static_cast<size_t>((rows + 255) / 256) * (K / 256) * 2048;
+}
+
+wush_status wush_transform_quant_mx_planes(wush_dtype xdt, int n, int d_in, const void* X, const float* Tx,
+                                           uint8_t* codes, uint8_t* planes, void* stream) {
+  wush_status st = check_common("wush_transform_quant_mx_planes", WUSH_MXFP4, n, d_in, X, codes, planes);
+  if (st != WUSH_OK) return st;
+  if (xdt != WUSH_F32 && xdt != WUSH_BF16) return wush::fail(WUSH_E_ARG, "wush_transform_quant_mx_planes: bad dtype");
+  if (d_in % 256 != 0) return wush::fail(WUSH_E_SHAPE, "wush_transform_quant_mx_planes: d_in must be a multiple of 256");
+  if (n > 0 && !Tx) return wush::fail(WUSH_E_ARG, "wush_transform_quant_mx_planes: needs a transform (Tx not NULL)");
+  return launch(kMXP, 32, xdt == WUSH_BF16, n, d_in, X, Tx, 0.0f, codes, planes, nullptr,
                 static_cast<hipStream_t>(stream));
 }
 

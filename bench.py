@@ -59,6 +59,9 @@ def parse():
                     help="identity | hadamard | wus | wush, or hd (the Hadamard-diagonal variant)")
     ap.add_argument("--batch", type=int, default=1, help="had256: batch 1..16")
     ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--row-major-scales", action="store_true",
+                    help="MXFP4: wush_transform_quant + wush_w4a4_gemm (scale pre-pass per call) instead of the "
+                         "plane-ordered scale path")
     ap.add_argument("--shared", type=int, default=0, metavar="G",
                     help="wus/wush: share one matrix per group of nblk/G adjacent blocks (shared-transform variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,7 +77,7 @@ def parse():
 class Layer:
     """One quantized linear layer, device resident, with `rotate` copies of its inputs."""
 
-    def __init__(self, wl, fmt, kind, rotate, W, torch, shared=0):
+    def __init__(self, wl, fmt, kind, rotate, W, torch, shared=0, planes=True):
         from synth.gen import make_weights, make_activations, bf16_bits
         self.wl, self.fmt, self.kind = wl, fmt, kind
         self.bs = W.BLOCK[fmt]
@@ -130,6 +133,17 @@ class Layer:
         self.xc = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device=dev)
         self.xsc = torch.empty((self.M, nblk), dtype=sdt, device=dev)
         self.Y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
+        # MXFP4 with a dense transform: scales in the matmul's plane order, the
+        # weights' converted once here, the activations' written by the step
+        self.planes = (planes and fmt == "mxfp4" and kind in ("hadamard", "wus", "wush") and not self.hd
+                       and self.group is None and self.K % 256 == 0)
+        if self.planes:
+            self.pa = torch.empty(W.wush_mxfp4_planes_bytes(self.M, self.K), dtype=torch.uint8, device=dev)
+            self.pb = []
+            for r in range(rotate):
+                pb = torch.empty(W.wush_mxfp4_planes_bytes(self.N, self.K), dtype=torch.uint8, device=dev)
+                W.wush_mxfp4_scale_planes(self.wsc[r], pb, self.K)
+                self.pb.append(pb)
         wsb = W.wush_w4a4_gemm_ws_bytes(fmt, self.M, self.N, self.K)
         self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev) if wsb else None
         self.x_elem_bytes = 2 if wl.dtype == "bf16" else 4
@@ -172,11 +186,16 @@ def run_layer_steps(layers, W, torch, steps, warmup, rotate):
                 W.wush_transform_quant_hd(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
             elif L.group is not None:
                 W.wush_transform_quant_shared(L.fmt, L.X[r], L.Tx, L.gdev, L.xc, L.xsc, g=L.x_g)
+            elif L.planes:
+                W.wush_transform_quant_mx_planes(L.X[r], L.Tx, L.xc, L.pa)
             else:
                 W.wush_transform_quant(L.fmt, L.X[r], L.Tx, L.xc, L.xsc, g=L.x_g)
             if ev is not None:
                 ev[li][1].record(stream)
-            W.wush_w4a4_gemm(L.fmt, L.xc, L.xsc, L.wc[r], L.wsc[r], L.Y, a_g=L.x_g, b_g=L.w_g, ws=L.ws)
+            if L.planes:
+                W.wush_w4a4_gemm_mx_planes(L.xc, L.pa, L.wc[r], L.pb[r], L.Y)
+            else:
+                W.wush_w4a4_gemm(L.fmt, L.xc, L.xsc, L.wc[r], L.wsc[r], L.Y, a_g=L.x_g, b_g=L.w_g, ws=L.ws)
             if ev is not None:
                 ev[li][2].record(stream)
 
@@ -349,7 +368,8 @@ def main():
         wls = [CONFIGS[args.workload]]
     fmt = args.fmt or wls[0].formats[0]
     kind = args.kind or ("wush" if "wush" in wls[0].kinds else wls[0].kinds[-1])
-    layers = [Layer(wl, fmt, kind, args.rotate, W, torch, shared=args.shared) for wl in wls]
+    layers = [Layer(wl, fmt, kind, args.rotate, W, torch, shared=args.shared, planes=not args.row_major_scales)
+              for wl in wls]
 
     ms_step, tq_ms, gm_ms = run_layer_steps(layers, W, torch, args.steps, args.warmup, args.rotate)
 
@@ -410,7 +430,8 @@ def main():
         "config": {"workload": wname, "transform": kind, "format": fmt,
                    "x_dtype": x_dtype, "tokens": layers[0].M,
                    "layers": [[L.K, L.N] for L in layers], "rotate_buffers": args.rotate,
-                   **({"shared_groups": args.shared} if layers[0].group is not None else {})},
+                   **({"shared_groups": args.shared} if layers[0].group is not None else {}),
+                   "mx_scale_layout": "planes" if layers[0].planes else "row-major"},
         "quant_GBps": round(tq_gbps, 1),
         "tq_us": round(tq_t * 1e6, 2),
         "gemm_us": round(gm_t * 1e6, 2),

@@ -117,6 +117,35 @@ wush_status wush_block_moments_dev(int bs, wush_dtype xdt, int n, int d_in, cons
 wush_status wush_build_transforms(wush_kind kind, int bs, int d_in, int d_out,
                                   const float* W, const float* Sx, float* Tx, float* Tw);
 
+/* MXFP4 scales in the matmul's plane order.  wush_w4a4_gemm first rewrites
+ * both operands' row-major E8M0 scales into the order its LDS stage keeps
+ * them (a pre-pass per call).  These calls let a caller do that once for the
+ * weights (wush_mxfp4_scale_planes, offline), have the activation step write
+ * that order directly (wush_transform_quant_mx_planes), and run the matmul on
+ * both (wush_w4a4_gemm_mx_planes): same kernels, bit-identical Y.
+ * Layout (K a multiple of 256): 2048 bytes per (256-row tile t, 256-wide K
+ * block kb) at (t * K/256 + kb) * 2048; within it, the scale of row
+ * r = row % 256 and group b = (k / 32) % 8 sits at
+ *   256 b + 16 (r % 16) + ((8 (r / 128) + (r / 16) % 8) XOR 8 (b % 2)).
+ * Bytes of rows past `rows` are zero after wush_mxfp4_scale_planes and left
+ * untouched by wush_transform_quant_mx_planes (the matmul never stores those
+ * rows).  wush_mxfp4_planes_bytes(rows, K) is the buffer size (0 for bad
+ * shapes).
+ *   wush_transform_quant_mx_planes: wush_transform_quant for MXFP4 with
+ *     scales written to `planes` in this layout; d_in % 256 == 0; Tx not NULL.
+ *   wush_w4a4_gemm_mx_planes: Y = A W^T as wush_w4a4_gemm (MXFP4) from the
+ *     plane-ordered scales; K % 256 == 0 and operands below 2 GiB, else
+ *     WUSH_E_SHAPE / WUSH_E_UNSUPPORTED.  Codes, planes and Y 16-byte aligned. */
+size_t wush_mxfp4_planes_bytes(int rows, int K);
+wush_status wush_mxfp4_scale_planes(int rows, int K, const uint8_t* scales, uint8_t* planes,
+                                    void* stream);
+wush_status wush_transform_quant_mx_planes(wush_dtype xdt, int n, int d_in, const void* X,
+                                           const float* Tx, uint8_t* codes, uint8_t* planes,
+                                           void* stream);
+wush_status wush_w4a4_gemm_mx_planes(int M, int N, int K, const uint8_t* a_codes,
+                                     const uint8_t* a_planes, const uint8_t* b_codes,
+                                     const uint8_t* b_planes, float* Y, void* stream);
+
 /* Shared-transform variant ([WUSH-news], paragraph on deployment limits:
  * similar blocks share one transform).  The caller assigns each block b a
  * group group[b] in [0, ngroups); every group must own a block.  A group's

@@ -252,6 +252,22 @@ def test_build_shared_matches_oracle_and_rejects_bad_groups():
     assert L.wush_nvfp4_global_scale_shared(0, 4, 128, None, None, 1, None, None, None) == W.WUSH_E_ARG
 
 
+def test_mx_planes_sizes_and_argument_checks():
+    L = W.lib
+    assert L.wush_mxfp4_planes_bytes(300, 512) == 2 * 2 * 2048
+    assert L.wush_mxfp4_planes_bytes(4096, 4096) == 16 * 16 * 2048
+    assert L.wush_mxfp4_planes_bytes(10, 384) == 0 and L.wush_mxfp4_planes_bytes(0, 512) == 0
+    assert L.wush_mxfp4_scale_planes(10, 384, None, None, None) == W.WUSH_E_SHAPE
+    assert L.wush_mxfp4_scale_planes(10, 512, None, None, None) == W.WUSH_E_ARG
+    assert L.wush_transform_quant_mx_planes(1, 4, 384, None, None, None, None, None) == W.WUSH_E_ARG
+    buf = np.zeros(8192, np.uint8)
+    p = (buf.ctypes.data + 15) // 16 * 16
+    assert L.wush_transform_quant_mx_planes(1, 4, 384, p, p, p, p, None) == W.WUSH_E_SHAPE
+    assert L.wush_transform_quant_mx_planes(1, 4, 512, p, None, p, p, None) == W.WUSH_E_ARG
+    assert L.wush_w4a4_gemm_mx_planes(4, 4, 384, p, p, p, p, p, None) == W.WUSH_E_SHAPE
+    assert L.wush_w4a4_gemm_mx_planes(4, 4, 512, None, p, p, p, p, None) == W.WUSH_E_ARG
+
+
 def test_block_moments_dev_checks_and_workspace_size():
     L = W.lib
     # 300 tokens: 2 chunks of up to 256; 5000: 20; 20000: capped at 64

@@ -76,6 +76,19 @@ def _layer_check(wl, fmt, kind, Wt, X, n_tok=48, n_w=48, seed=0):
     Y = torch.empty((n, d_out), dtype=torch.float32, device=DEV)
     W.wush_w4a4_gemm(fmt, xc, xs, wc, wsc, Y, a_g=g_x or 1.0, b_g=gw_dev)
     torch.cuda.synchronize()
+    if fmt == "mxfp4" and not hd and kind != "identity" and d_in % 256 == 0:
+        # the plane-ordered scale path bench.py times: the same codes and a bit-identical Y
+        xc2 = torch.empty_like(xc)
+        pa = torch.empty(W.wush_mxfp4_planes_bytes(n, d_in), dtype=torch.uint8, device=DEV)
+        pb = torch.empty(W.wush_mxfp4_planes_bytes(d_out, d_in), dtype=torch.uint8, device=DEV)
+        W.wush_transform_quant_mx_planes(x_dev(X, wl.dtype), to_dev(Tx), xc2, pa)
+        W.wush_mxfp4_scale_planes(wsc, pb, d_in)
+        Y2 = torch.empty_like(Y)
+        W.wush_w4a4_gemm_mx_planes(xc2, pa, wc, pb, Y2)
+        torch.cuda.synchronize()
+        assert torch.equal(xc2, xc)
+        assert torch.equal(Y2.view(torch.int32), Y.view(torch.int32))
+        del xc2, pa, pb, Y2
 
     # oracle on the sampled rows
     rc, rs = tq(Tx, X[tok], g_x)

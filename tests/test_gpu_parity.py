@@ -147,6 +147,50 @@ def test_transform_quant_and_pack_shared_bit_exact(fmt, dtype):
         assert np.array_equal(scales_np(sc, fmt), ws_) and np.array_equal(host(codes), wc), (fmt, n, d_in)
 
 
+def _planes_np(S):
+    """Row-major E8M0 scales [rows][K/32] -> the matmul's plane order (layout of wush.h)."""
+    rows, G = S.shape
+    nb, tiles = G // 8, (rows + 255) // 256
+    r = np.arange(rows)[:, None]
+    gi = np.arange(G)[None, :]
+    rr, b = r % 256, gi % 8
+    pos = (8 * (rr // 128) + (rr // 16) % 8) ^ (8 * (b % 2))
+    off = ((r // 256) * nb + gi // 8) * 2048 + b * 256 + (rr % 16) * 16 + pos
+    P = np.zeros(tiles * nb * 2048, np.uint8)
+    P[off.ravel()] = S.ravel()
+    return P
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mx_planes_path_matches_row_major_path(dtype):
+    n, d_in, d_out = 300, 512, 320
+    Wt, X = random_case(600, n, d_in, d_out, dtype=dtype)
+    Tx, Tw, _, rc, rs = _oracle_tq("mxfp4", "wush", X, Wt)
+    xd = x_dev(X, dtype)
+    codes = torch.empty((n, d_in // 2), dtype=torch.uint8, device=DEV)
+    pa = torch.zeros(W.wush_mxfp4_planes_bytes(n, d_in), dtype=torch.uint8, device=DEV)
+    W.wush_transform_quant_mx_planes(xd, to_dev(Tx), codes, pa)
+    wc = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=DEV)
+    wsc = torch.empty((d_out, d_in // 32), dtype=torch.uint8, device=DEV)
+    W.wush_pack_weights("mxfp4", to_dev(Wt), to_dev(Tw), wc, wsc)
+    pb = torch.empty(W.wush_mxfp4_planes_bytes(d_out, d_in), dtype=torch.uint8, device=DEV)
+    W.wush_mxfp4_scale_planes(wsc, pb, d_in)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(codes), rc)
+    assert np.array_equal(host(pa), _planes_np(rs))                  # padding rows stay zero
+    assert np.array_equal(host(pb), _planes_np(host(wsc)))
+    # the matmul on plane-ordered scales equals the row-major call bit for bit
+    xc = torch.empty_like(codes)
+    xs = torch.empty((n, d_in // 32), dtype=torch.uint8, device=DEV)
+    W.wush_transform_quant("mxfp4", xd, to_dev(Tx), xc, xs)
+    Y0 = torch.empty((n, d_out), dtype=torch.float32, device=DEV)
+    Y1 = torch.empty_like(Y0)
+    W.wush_w4a4_gemm("mxfp4", xc, xs, wc, wsc, Y0)
+    W.wush_w4a4_gemm_mx_planes(codes, pa, wc, pb, Y1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Y0).view(np.uint32), host(Y1).view(np.uint32))
+
+
 def _edge_inputs(d_in):
     rng = np.random.default_rng(77)
     X = rng.standard_normal((9, d_in)).astype(np.float32)
