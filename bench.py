@@ -386,9 +386,10 @@ def main():
     # dominant kernel by measured time
     dom_gemm = gm_t >= tq_t
     wname = "+".join(L.wl.name for L in layers)
-    roof_gemm = {"kernel": "wush_w4a4_gemm", "bound": "mfma", "achieved": round(gemm_achieved, 2),
+    gemm_name = "wush_w4a4_gemm_mx_planes" if layers[0].planes else "wush_w4a4_gemm"
+    roof_gemm = {"kernel": gemm_name, "bound": "mfma", "achieved": round(gemm_achieved, 2),
                  "peak": gemm_peak, "unit": "TFLOP/s", "frac": round(gemm_achieved / gemm_peak, 4),
-                 "traffic": measured_traffic("wush_w4a4_gemm", wname) if fmt == "mxfp4" else None,
+                 "traffic": measured_traffic(gemm_name, wname) if fmt == "mxfp4" else None,
                  "algorithmic_bytes": round(sum(L.gemm_bytes() for L in layers) / len(layers)),
                  "avg_us": round(gm_t * 1e6 / len(layers), 2)}
     if fmt == "int4":
@@ -398,7 +399,8 @@ def main():
                           "unit": "Top/s", "frac": round(rescale / VALU_TOPS, 4),
                           "int8_TOPS": round(gemm_achieved, 2), "int8_frac": round(gemm_achieved / INT8_TOPS, 4)})
     tq_name = ("wush_transform_quant_hd" if layers[0].hd else
-               "wush_transform_quant_shared" if layers[0].group is not None else "wush_transform_quant")
+               "wush_transform_quant_shared" if layers[0].group is not None else
+               "wush_transform_quant_mx_planes" if layers[0].planes else "wush_transform_quant")
     # dense transforms: fp32 matrix cores; the diagonal variant: vector ALU
     tq_peak, tq_bound = (VALU_FP32_TFLOPS, "alu") if layers[0].hd else (MFMA_FP32_TFLOPS, "mfma")
     t_alu = tq_flops / (tq_peak * 1e12)
