@@ -45,6 +45,8 @@ _SIGS = {
     "wush_transform_apply": ([_i, _i, _i, _i, _p, _p, _p, _p], _i),
     "wush_build_shared": ([_i, _i, _i, _i, _p, _p, _i, _p, _p, _p], _i),
     "wush_mxfp4_planes_bytes": ([_i, _i], _sz),
+    "wush_build_transforms_dev_ws_bytes": ([_i, _i], _sz),
+    "wush_build_transforms_dev": ([_i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
     "wush_mxfp4_scale_planes": ([_i, _i, _p, _p, _p], _i),
     "wush_transform_quant_mx_planes": ([_i, _i, _i, _p, _p, _p, _p, _p], _i),
     "wush_w4a4_gemm_mx_planes": ([_i, _i, _i, _p, _p, _p, _p, _p, _p], _i),
@@ -205,6 +207,21 @@ def wush_pack_weights_shared(fmt, W, Tw, group, codes, scales, stream=None):
                                         _ptr(codes), _ptr(scales), ctypes.byref(g), _stream(stream)),
            "wush_pack_weights_shared")
     return g.value
+
+
+def wush_build_transforms_dev_ws_bytes(bs, d_in):
+    return lib.wush_build_transforms_dev_ws_bytes(bs, d_in)
+
+
+def wush_build_transforms_dev(kind, bs, W, Sx, Tx, Tw, ws=None, stream=None):
+    """Device tensors: W [d_out][d_in] f32, Sx [nblk][bs][bs] f32 -> Tx, Tw [nblk][bs][bs] f32 (synchronises)."""
+    import torch
+    d_out, d_in = W.shape
+    need = lib.wush_build_transforms_dev_ws_bytes(bs, d_in)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=Tx.device)
+    _check(lib.wush_build_transforms_dev(KINDS[kind], bs, d_in, d_out, _ptr(W), _ptr(Sx), _ptr(Tx), _ptr(Tw), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)), "wush_build_transforms_dev")
 
 
 def wush_mxfp4_planes_bytes(rows, K):

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwush.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-HIP_SOURCES = ["transform_quant.hip", "gemm_mxfp4.hip", "gemm_nv_int4.hip", "gemm_nvfp4.hip", "gemm_int4.hip", "gemm.hip", "loss.hip", "had256.hip", "moments.hip"]
+HIP_SOURCES = ["transform_quant.hip", "gemm_mxfp4.hip", "gemm_nv_int4.hip", "gemm_nvfp4.hip", "gemm_int4.hip", "gemm.hip", "loss.hip", "had256.hip", "moments.hip", "builder_dev.hip"]
 CXX_SOURCES = ["builder.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

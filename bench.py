@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_up",
-                    choices=["qwen3_8b_up", "tiny", "square_sweep", "qwen3_14b", "had256", "moments"])
+                    choices=["qwen3_8b_up", "tiny", "square_sweep", "qwen3_14b", "had256", "moments", "build"])
     ap.add_argument("--fmt", default=None, help="square_sweep: mxfp4 | nvfp4 | int4")
     ap.add_argument("--kind", default=None,
                     help="identity | hadamard | wus | wush, or hd (the Hadamard-diagonal variant)")
@@ -361,6 +361,8 @@ def main():
         return bench_had256(args, W, torch)
     if args.workload == "moments":
         return bench_moments(args, W, torch)
+    if args.workload == "build":
+        return bench_build(args, W, torch)
 
     if args.workload == "qwen3_14b":
         wls = [CONFIGS["qwen3_14b_up"], CONFIGS["qwen3_14b_down"]]
@@ -523,6 +525,47 @@ def bench_moments(args, W, torch):
            "roofline": {"kernel": "wush_block_moments_dev", "bound": "alu", "achieved": round(tflops, 3),
                         "peak": FP64_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP64_TFLOPS, 4),
                         "traffic": None, "avg_us": round(ms * 1e3, 2)}}
+    print(json.dumps(out), flush=True)
+
+
+def bench_build(args, W, torch):
+    """The offline transform builder on the GPU for the Qwen3-8B up-projection (WUSH, bs 32), next to the host one."""
+    from synth.gen import CONFIGS, make_weights, make_activations
+    wl = CONFIGS["qwen3_8b_up"]
+    Wt, X = make_weights(wl), make_activations(wl)
+    d_out, d_in = Wt.shape
+    bs, nblk = 32, d_in // 32
+    Sx = np.empty((nblk, bs, bs), np.float32)
+    W.wush_block_moments(bs, X, Sx)
+    dev = "cuda"
+    Wd, Sd = torch.from_numpy(Wt).to(dev), torch.from_numpy(Sx).to(dev)
+    Tx = torch.empty((nblk, bs, bs), dtype=torch.float32, device=dev)
+    Tw = torch.empty_like(Tx)
+    ws = torch.empty(W.wush_build_transforms_dev_ws_bytes(bs, d_in), dtype=torch.uint8, device=dev)
+    for _ in range(max(1, args.warmup // 5)):
+        W.wush_build_transforms_dev("wush", bs, Wd, Sd, Tx, Tw, ws=ws)
+    steps = max(1, args.steps // 10)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        W.wush_build_transforms_dev("wush", bs, Wd, Sd, Tx, Tw, ws=ws)   # synchronises
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    hx, hw = np.empty((nblk, bs, bs), np.float32), np.empty((nblk, bs, bs), np.float32)
+    t0 = time.perf_counter()
+    W.wush_build_transforms("wush", bs, Wt, Sx, hx, hw)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    same = bool(np.array_equal(Tx.cpu().numpy(), hx) and np.array_equal(Tw.cpu().numpy(), hw))
+    moment_flops = 2.0 * d_out * nblk * bs * (bs + 1) / 2        # the weight moments dominate the arithmetic
+    tflops = moment_flops / (ms / 1e3) / 1e12
+    out = {"metric": "transform builder blocks/s (offline, fp64)", "value": round(nblk / (ms / 1e3), 1),
+           "unit": "blocks/s", "n_gpus": 1, "steps": steps, "warmup": max(1, args.warmup // 5),
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f64", "data": "synthetic",
+           "config": {"workload": wl.name + "-build", "d_out": d_out, "d_in": d_in, "bs": bs, "kind": "wush"},
+           "host_builder_ms": round(host_ms, 2), "host_threads": os.cpu_count(), "identical_to_host": same,
+           "roofline": {"kernel": "wush_build_transforms_dev", "bound": "alu", "achieved": round(tflops, 4),
+                        "peak": FP64_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP64_TFLOPS, 5),
+                        "traffic": None, "avg_us": round(ms * 1e3, 1)}}
     print(json.dumps(out), flush=True)
 
 

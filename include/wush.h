@@ -146,6 +146,23 @@ wush_status wush_w4a4_gemm_mx_planes(int M, int N, int K, const uint8_t* a_codes
                                      const uint8_t* a_planes, const uint8_t* b_codes,
                                      const uint8_t* b_planes, float* Y, void* stream);
 
+/* wush_build_transforms on the GPU ([WUSH-news] deployment paragraph: the
+ * per-block computations are independent and parallel).  Same construction,
+ * operation order and fp64 arithmetic as the host call, so the two produce
+ * the same matrices; W and Sx (for instance from wush_block_moments_dev) stay
+ * on the device.  Offline: one thread per block for the factorisations.
+ *   W, Sx   device, as in wush_build_transforms (unused for IDENTITY/HADAMARD).
+ *   Tx, Tw  device out, [d_in/bs][bs][bs] fp32.
+ *   ws      device workspace of wush_build_transforms_dev_ws_bytes(bs, d_in)
+ *           bytes (fp64 weight moments and per-block status), 16-byte aligned.
+ * Synchronises `stream` (the damping verdicts come back to the host).
+ * Errors: those of wush_build_transforms, plus WUSH_E_ARG for a missing or
+ * short workspace and WUSH_E_HIP. */
+size_t wush_build_transforms_dev_ws_bytes(int bs, int d_in);
+wush_status wush_build_transforms_dev(wush_kind kind, int bs, int d_in, int d_out,
+                                      const float* W, const float* Sx, float* Tx, float* Tw,
+                                      void* ws, size_t ws_bytes, void* stream);
+
 /* Shared-transform variant ([WUSH-news], paragraph on deployment limits:
  * similar blocks share one transform).  The caller assigns each block b a
  * group group[b] in [0, ngroups); every group must own a block.  A group's

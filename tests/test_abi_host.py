@@ -252,6 +252,21 @@ def test_build_shared_matches_oracle_and_rejects_bad_groups():
     assert L.wush_nvfp4_global_scale_shared(0, 4, 128, None, None, 1, None, None, None) == W.WUSH_E_ARG
 
 
+def test_build_transforms_dev_workspace_and_argument_checks():
+    L = W.lib
+    assert L.wush_build_transforms_dev_ws_bytes(32, 4096) == 128 * 32 * 32 * 8 + 512
+    assert L.wush_build_transforms_dev_ws_bytes(16, 48) == 3 * 16 * 16 * 8 + 256
+    assert L.wush_build_transforms_dev_ws_bytes(24, 48) == 0 and L.wush_build_transforms_dev_ws_bytes(32, 48) == 0
+    buf = np.zeros(1 << 16, np.uint8)
+    p = (buf.ctypes.data + 15) // 16 * 16
+    assert L.wush_build_transforms_dev(9, 32, 64, 4, p, p, p, p, p, 1 << 15, None) == W.WUSH_E_ARG
+    assert L.wush_build_transforms_dev(3, 24, 48, 4, p, p, p, p, p, 1 << 15, None) == W.WUSH_E_SHAPE
+    assert L.wush_build_transforms_dev(3, 32, 64, 4, p, p, None, p, p, 1 << 15, None) == W.WUSH_E_ARG
+    assert L.wush_build_transforms_dev(3, 32, 64, 4, None, p, p, p, p, 1 << 15, None) == W.WUSH_E_ARG
+    assert L.wush_build_transforms_dev(3, 32, 64, 4, p, p, p, p, p, 100, None) == W.WUSH_E_ARG   # short workspace
+    assert L.wush_build_transforms_dev(3, 32, 64, 4, p, p, p, p, None, 1 << 15, None) == W.WUSH_E_ARG
+
+
 def test_mx_planes_sizes_and_argument_checks():
     L = W.lib
     assert L.wush_mxfp4_planes_bytes(300, 512) == 2 * 2 * 2048

@@ -147,6 +147,35 @@ def test_transform_quant_and_pack_shared_bit_exact(fmt, dtype):
         assert np.array_equal(scales_np(sc, fmt), ws_) and np.array_equal(host(codes), wc), (fmt, n, d_in)
 
 
+@pytest.mark.parametrize("bs", [32, 16])
+def test_build_transforms_on_device_equals_host_builder(bs):
+    # same construction and fp64 operation order on both sides: identical matrices
+    Wt, X = random_case(700 + bs, 300, 8 * bs, 96)
+    Wt[:, bs:2 * bs] *= np.float32(1e-3)                    # a badly scaled block
+    rng = np.random.default_rng(bs)
+    Wt[:, 2 * bs:3 * bs] = np.outer(rng.standard_normal(Wt.shape[0]),
+                                    rng.standard_normal(bs)).astype(np.float32)   # rank one: the damping ladder
+    Sx = tr.activation_moments(X, bs).astype(np.float32)
+    nblk = Wt.shape[1] // bs
+    for kind in ("identity", "hadamard", "wus", "wush"):
+        hx = np.empty((nblk, bs, bs), np.float32)
+        hw = np.empty_like(hx)
+        W.wush_build_transforms(kind, bs, Wt, Sx, hx, hw)
+        dx = torch.empty((nblk, bs, bs), dtype=torch.float32, device=DEV)
+        dw = torch.empty_like(dx)
+        W.wush_build_transforms_dev(kind, bs, to_dev(Wt), to_dev(Sx), dx, dw)
+        ex, ew = host(dx), host(dw)
+        ulp = lambda a, b: np.abs(a.view(np.int32).astype(np.int64) - b.view(np.int32).astype(np.int64)).max()
+        assert np.array_equal(ex.view(np.uint32), hx.view(np.uint32)), (kind, ulp(ex, hx))
+        assert np.array_equal(ew.view(np.uint32), hw.view(np.uint32)), (kind, ulp(ew, hw))
+    Wz = Wt.copy()
+    Wz[:, :bs] = 0.0                                        # all-zero block: no Cholesky factor at any rung
+    dx = torch.empty((nblk, bs, bs), dtype=torch.float32, device=DEV)
+    with pytest.raises(W.WushError) as e:
+        W.wush_build_transforms_dev("wush", bs, to_dev(Wz), to_dev(Sx), dx, torch.empty_like(dx))
+    assert e.value.status == W.WUSH_E_NUMERIC
+
+
 def _planes_np(S):
     """Row-major E8M0 scales [rows][K/32] -> the matmul's plane order (layout of wush.h)."""
     rows, G = S.shape
