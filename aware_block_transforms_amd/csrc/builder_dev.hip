@@ -267,7 +267,7 @@ wush_status wush_build_transforms_dev(wush_kind kind, int bs, int d_in, int d_ou
                      Sx, Tx, Tw, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "wush_build_transforms_dev launch: %s", hipGetErrorString(e));
-  // the damping verdicts come back to the host (this call synchronises the stream)
+  // the damping results come back to the host (this call synchronises the stream)
   int* hs = new int[nblk];
   e = hipMemcpyAsync(hs, status, sizeof(int) * nblk, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);

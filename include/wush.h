@@ -155,7 +155,7 @@ wush_status wush_w4a4_gemm_mx_planes(int M, int N, int K, const uint8_t* a_codes
  *   Tx, Tw  device out, [d_in/bs][bs][bs] fp32.
  *   ws      device workspace of wush_build_transforms_dev_ws_bytes(bs, d_in)
  *           bytes (fp64 weight moments and per-block status), 16-byte aligned.
- * Synchronises `stream` (the damping verdicts come back to the host).
+ * Synchronises `stream` (the damping results come back to the host).
  * Errors: those of wush_build_transforms, plus WUSH_E_ARG for a missing or
  * short workspace and WUSH_E_HIP. */
 size_t wush_build_transforms_dev_ws_bytes(int bs, int d_in);
