@@ -281,9 +281,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves
   const int nblk = d_in / BS;
   const int blk = blockIdx.x * kWavesPerGroup + wave;
   if (blk >= nblk) return;                       // wave-uniform
-  const float* __restrict__ Tb = IDENT ? nullptr : T + static_cast<size_t>(blk) * BS * BS;
-  (void)tmap;
-  (void)ngroups;
+  // the block's matrix, or with a group map its group's (ids clamped to the table)
+  const int tsel = tmap ? min(max(tmap[blk], 0), ngroups - 1) : blk;
+  const float* __restrict__ Tb = IDENT ? nullptr : T + static_cast<size_t>(tsel) * BS * BS;
   const int tok0 = blockIdx.y * (2 * kWave) + lane, tok1 = tok0 + kWave;
   const bool v0 = tok0 < n, v1 = tok1 < n;
   uint32_t run_max = 0;
@@ -662,10 +662,13 @@ __global__ void fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
 using KernelFn = void (*)(const void*, const float*, int, int, float, uint8_t*, void*, uint32_t*, const int*, int);
 
+// bf16 x: the matrix-core kernel.  fp32 x still reads every fourth element
+// with scattered dword loads there (no LDS transpose yet), which is slower
+// than the vector-ALU kernel, so fp32 x keeps the latter.
 template <int BS, int FMT>
 KernelFn pick(bool bf16, bool ident) {
   if (bf16) return ident ? tq_kernel<BS, FMT, true, true> : tq_mfma_kernel<BS, FMT, true>;
-  return ident ? tq_kernel<BS, FMT, false, true> : tq_mfma_kernel<BS, FMT, false>;
+  return ident ? tq_kernel<BS, FMT, false, true> : tq_kernel<BS, FMT, false, false>;
 }
 
 KernelFn select_kernel(int fmt, int bs, bool bf16, bool ident) {
@@ -700,7 +703,8 @@ wush_status launch(int fmt, int bs, bool bf16, int n, int d_in, const void* X, c
   KernelFn k = select_kernel(fmt, bs, bf16, T == nullptr);
   if (!k) return wush::fail(WUSH_E_UNSUPPORTED, "transform_quant: no kernel for fmt=%d bs=%d", fmt, bs);
   const int nblk = d_in / bs;
-  const int per_wave = !T ? kTokensPerWave
+  const bool mfma = T && (bf16 || fmt == kApply || fmt == kMXP);
+  const int per_wave = !mfma ? kTokensPerWave
                        : kMfmaUnits * (bs == 32 ? (bf16 ? XUnit<32, true>::kRows : XUnit<32, false>::kRows)
                                                 : (bf16 ? XUnit<16, true>::kRows : XUnit<16, false>::kRows));
   dim3 grid((nblk + kWavesPerGroup - 1) / kWavesPerGroup, (n + per_wave - 1) / per_wave);
