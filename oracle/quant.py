@@ -21,6 +21,10 @@ Pinned arithmetic (the pages leave it open; codes depend on every bit):
               q_i = clamp(rint_even(f32(y_i r)), -7, 7) stored as q & 0xF;
               NaN/Inf block -> scale 0x7E00, codes 0.
 * packing:    byte j of a row holds code 2j in its low nibble, 2j+1 in its high.
+
+The nibble order and the NVFP4 divisor 6 * 448 are format choices: the pages
+fix neither.  Both are pinned by hand-derived bytes and scales in
+tests/golden/packing.json, which do not pass through this module's unpack.
 """
 
 import numpy as np

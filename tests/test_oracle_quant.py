@@ -205,3 +205,76 @@ def test_transform_quant_hd_is_apply_then_quantize():
     c1, s1 = quant.transform_quant_hd("mxfp4", d, x)
     c2, s2 = quant.quant_mxfp4(quant.apply_hd(d, x, 32))
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+# ----------------------------------------------------------------------------- byte-layout pins
+# Hand-derived bytes (tests/golden/packing.json): they do not go through the
+# oracle's own unpack, so a swapped nibble order or a different NVFP4 tensor
+# scale divisor fails here even though the matmul is invariant to both.
+
+def _packing_golden():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "packing.json")) as f:
+        return json.load(f)
+
+
+def test_pack_nibbles_hand_rows():
+    gold = _packing_golden()
+    for row in gold["nibble_rows"]:
+        got = quant.pack_nibbles(np.array([row["codes"]], np.uint8))
+        assert list(got[0]) == row["bytes"]
+        back = quant.unpack_nibbles(np.array([row["bytes"]], np.uint8))
+        assert list(back[0]) == row["codes"]
+
+
+def _block(spec, bs):
+    y = np.full((1, bs), spec["rest"], np.float32)
+    y[0, :len(spec["values_head"])] = spec["values_head"]
+    return y
+
+
+def test_mxfp4_block_hand_bytes():
+    gold = _packing_golden()["mxfp4_block"]
+    codes, scales = quant.quant_mxfp4(_block(gold, 32))
+    assert int(scales[0, 0]) == gold["scale_byte"]
+    head = gold["bytes_head"]
+    assert list(codes[0, :len(head)]) == head
+    assert np.all(codes[0, len(head):] == 0)
+
+
+def test_int4_block_hand_bytes():
+    gold = _packing_golden()["int4_block"]
+    codes, scales = quant.quant_int4(_block(gold, 32))
+    assert int(scales[0, 0]) == gold["scale_fp16_bits"]
+    head = gold["bytes_head"]
+    assert list(codes[0, :len(head)]) == head
+    assert np.all(codes[0, len(head):] == 0)
+
+
+def test_nvfp4_tensor_scale_hand_values():
+    gold = _packing_golden()
+    rng = np.random.default_rng(11)
+    for case in gold["nvfp4_tensor_scale"]:
+        y = rng.uniform(-1, 1, (8, 64)).astype(np.float32) * np.float32(case["amax"] / 2)
+        y[3, 17] = -case["amax"]
+        g = quant.nvfp4_tensor_scale(y)
+        assert g.dtype == np.float32 and float(g) == case["g"]
+        # the block that holds the tensor maximum takes the largest finite E4M3 scale
+        _, scales = quant.quant_nvfp4(y, g)
+        assert int(scales[3, 17 // 16]) == gold["nvfp4_max_block_scale_byte"]
+        assert np.all(scales <= gold["nvfp4_max_block_scale_byte"])
+
+
+def test_nvfp4_max_block_scale_at_any_amax():
+    # for any tensor the block holding max|y| is scaled to 448 (byte 0x7E) and its
+    # largest value encodes as the top E2M1 level, 6
+    gold = _packing_golden()
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        y = (rng.standard_normal((4, 48)) * np.exp(rng.uniform(-20, 20))).astype(np.float32)
+        g = quant.nvfp4_tensor_scale(y)
+        codes, scales = quant.quant_nvfp4(y, g)
+        r, c = np.unravel_index(np.argmax(np.abs(y)), y.shape)
+        assert int(scales[r, c // 16]) == gold["nvfp4_max_block_scale_byte"]
+        assert int(quant.unpack_nibbles(codes)[r, c]) & 7 == 7
