@@ -52,8 +52,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen3_8b_up",
-                    choices=["qwen3_8b_up", "tiny", "square_sweep", "qwen3_14b", "had256", "moments", "build"])
+    ap.add_argument("--workload", default="qwen3_14b",
+                    choices=["qwen3_14b", "qwen3_8b_up", "tiny", "square_sweep", "had256", "moments", "build",
+                             "mfma_ceiling"],
+                    help="default: the Qwen3-14B MLP pair (up 5120->17408, down 17408->5120) at 16384 tokens, "
+                         "the largest configuration that fits one GPU")
     ap.add_argument("--fmt", default=None, help="square_sweep: mxfp4 | nvfp4 | int4")
     ap.add_argument("--kind", default=None,
                     help="identity | hadamard | wus | wush, or hd (the Hadamard-diagonal variant)")
@@ -65,7 +68,10 @@ def parse():
     ap.add_argument("--shared", type=int, default=0, metavar="G",
                     help="wus/wush: share one matrix per group of nblk/G adjacent blocks (shared-transform variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0, help="target wall time of the oracle sample")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes for the oracle's transform+quantize leg (default: the host cores this process "
+                         "may use, at most 16)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer --steps times (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -77,14 +83,12 @@ def parse():
 class Layer:
     """One quantized linear layer, device resident, with `rotate` copies of its inputs."""
 
-    def __init__(self, wl, fmt, kind, rotate, W, torch, shared=0, planes=True):
-        from synth.gen import make_weights, make_activations, bf16_bits
+    def __init__(self, wl, fmt, kind, rotate, W, torch, Wt, X, shared=0, planes=True):
+        from synth.gen import bf16_bits
         self.wl, self.fmt, self.kind = wl, fmt, kind
         self.bs = W.BLOCK[fmt]
         self.M, self.K, self.N = wl.n, wl.d_in, wl.d_out
         t0 = time.time()
-        Wt = make_weights(wl)
-        X = make_activations(wl)
         nblk = self.K // self.bs
         # offline: moments and transforms on the host (library C++ builder)
         Sx = np.empty((nblk, self.bs, self.bs), np.float32)
@@ -173,6 +177,19 @@ class Layer:
         return (self.M + self.N) * self.K * (0.5 + sb) + self.M * self.N * 4
 
 
+def tq_engine(L):
+    """(bound, peak TFLOP/s) of the unit the layer's transform+quantize kernel computes on.
+
+    Mirrors the library's dispatch: the dense transforms run on the fp32 matrix
+    cores (v_mfma_f32_16x16x4_f32) for bf16 and fp32 activations alike; the
+    Hadamard-diagonal variant runs one product and log2(bs) adds per element
+    on the vector ALU (one lane operation each); identity has no arithmetic.
+    """
+    if L.hd:
+        return "alu", VALU_TOPS
+    return "mfma", MFMA_FP32_TFLOPS
+
+
 def run_layer_steps(layers, W, torch, steps, warmup, rotate):
     """Warm up, then time `steps` steps; per-kernel HIP events on the launch stream."""
     stream = torch.cuda.current_stream()
@@ -226,104 +243,149 @@ def run_layer_steps(layers, W, torch, steps, warmup, rotate):
 # ----------------------------------------------------------------------------- HBM traffic
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, layer_names):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
 
-    The summary records the kernel source's sha256 prefix at measurement time;
-    once the source has changed (or for another workload) the figure no longer
-    describes this kernel and None is reported.
+    Records are keyed "<entry point>@<layer workload>" and hold the kernel
+    source's sha256 prefix at measurement time; once the source has changed
+    the figure no longer describes this kernel and None is reported.  With
+    several layers in the step the figure is the mean over their launches
+    (matching `achieved`, which is per launch on average too).
     """
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
-            rec = json.load(f)[kernel]
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+            recs = json.load(f)
+        total = 0.0
+        for name in layer_names:
+            rec = recs[kernel + "@" + name]
+            with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest()[:16] != rec["sha256_prefix"]:
+                    return None
+            total += (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024
     except (OSError, KeyError, ValueError):
         return None
-    if sha != rec["sha256_prefix"] or workload != rec["workload"]:
-        return None
-    return round((rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024)
+    return round(total / len(layer_names))
 
 
 # ----------------------------------------------------------------------------- CPU baseline
 
 
-def cpu_threads():
+def host_workers(requested=0):
+    """Processes for the oracle's pooled leg: the cores this process may run on, at most 16."""
     try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        n = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
-        return int(n)
-    except Exception:
-        return 1
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(requested or 16, n))
 
 
-def cpu_baseline(L, target_s):
-    """Oracle time for the same step, measured on a bounded sample and scaled to TFLOP/s.
+# State the forked workers of the oracle's transform+quantize leg read (set
+# before the pool is created, inherited by fork; never touched by the GPU path).
+_CPU_LEG = {}
 
-    transform+quantize: `mt` tokens of the real activations with the real transforms;
-    matmul: the oracle's decode + fp64 product of `ms` token rows against `ns` weight
-    rows (those weight codes are prepared by the oracle outside the timed region).
-    Step time = per-token tq time * M + per-flop GEMM time * 2MNK.
+
+def _oracle_tq_rows(bounds):
+    lo, hi = bounds
+    st = _CPU_LEG
+    return st["fn"](st["T"], st["rows"][lo:hi], st["g"])
+
+
+def _oracle_tq_pool(fn, T, rows, g, workers):
+    """Oracle transform+quantize of `rows` split over `workers` forked processes."""
+    import multiprocessing as mp
+    _CPU_LEG.update(fn=fn, T=T, rows=rows, g=g)
+    n = rows.shape[0]
+    step = -(-n // workers)
+    chunks = [(lo, min(n, lo + step)) for lo in range(0, n, step)]
+    with mp.get_context("fork").Pool(len(chunks)) as pool:
+        parts = pool.map(_oracle_tq_rows, chunks)
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def cpu_baseline(cases, fmt, kind, shared, target_s, workers):
+    """The oracle timed on a bounded sample of the same step, scaled to TFLOP/s.
+
+    Runs before the process touches the GPU (its transform+quantize leg forks
+    worker processes).  Per layer: the oracle builds its own transforms from
+    the seeded inputs (untimed); transform+quantize of `mt` activation rows
+    runs over `workers` processes (wall time); the matmul leg decodes and
+    multiplies `ms` of those rows against `ns` weight rows in fp64 with
+    `workers` BLAS threads (weight codes prepared untimed).  The step time is
+    the sum over layers of (tq wall per row x M) + (matmul time per flop x 2MNK).
     """
+    from threadpoolctl import threadpool_limits
     from oracle import quant, gemm, transforms
-    Wt, X, _, _ = L.host
-    ident = L.kind == "identity"
-    # the oracle builds its own transforms (untimed)
-    Sx = transforms.activation_moments(X, L.bs).astype(np.float32)
-    if L.hd:
-        Tx, Tw, _, _ = transforms.build_hd(Wt, Sx, L.bs)
+    bs = {"mxfp4": 32, "nvfp4": 16, "int4": 32}[fmt]
+    step_s, flops, notes = 0.0, 0.0, []
+    for wl, Wt, X in cases:
+        M, K, N = X.shape[0], X.shape[1], Wt.shape[0]
+        with threadpool_limits(workers):
+            Sx = transforms.activation_moments(X, bs).astype(np.float32)
+            if kind == "hd":
+                Tx, Tw, _, _ = transforms.build_hd(Wt, Sx, bs)
 
-        def tq(T, rows, gg):
-            return quant.transform_quant_hd(L.fmt, T, rows, g=gg)
-    elif L.group is not None:
-        Tg, Twg, _, _ = transforms.build_shared(L.kind, Wt, Sx, L.bs, L.group, L.ngroups)
-        Tx, Tw = transforms.expand_shared(Tg, L.group), transforms.expand_shared(Twg, L.group)
+                def tq(T, rows, gg):
+                    return quant.transform_quant_hd(fmt, T, rows, g=gg)
+                apply = quant.apply_hd
+            elif shared and kind in ("wus", "wush"):
+                nblk = K // bs
+                group = (np.arange(nblk) * shared // nblk).astype(np.int32)
+                Tg, Twg, _, _ = transforms.build_shared(kind, Wt, Sx, bs, group, shared)
+                Tx, Tw = transforms.expand_shared(Tg, group), transforms.expand_shared(Twg, group)
 
-        def tq(T, rows, gg):
-            return quant.transform_quant(L.fmt, T, rows, g=gg)
-    else:
-        Tx, Tw, _, _ = transforms.build_transforms(L.kind, Wt, Sx, L.bs)
+                def tq(T, rows, gg):
+                    return quant.transform_quant(fmt, T, rows, g=gg)
+                apply = quant.apply_transform
+            else:
+                Tx, Tw, _, _ = transforms.build_transforms(kind, Wt, Sx, bs)
+                ident = kind == "identity"
 
-        def tq(T, rows, gg):
-            return quant.transform_quant(L.fmt, T, rows, g=gg, identity=ident)
-    g = None
-    if L.fmt == "nvfp4":
-        g = L.x_g
-    # size the sample to roughly target_s seconds of work (calibrate on a small run)
-    mt = 8
-    t0 = time.perf_counter()
-    tq(Tx, X[:mt], g)
-    per_tok = (time.perf_counter() - t0) / mt
-    mt = int(max(8, min(L.M, 0.5 * target_s / max(per_tok, 1e-9))))
-    t0 = time.perf_counter()
-    ca, sa = tq(Tx, X[:mt], g)
-    t_tq = time.perf_counter() - t0
-    ns = min(L.N, 1024)
-    wg = None
-    if L.fmt == "nvfp4":
-        wg = L.w_g
-    cw, sw = tq(Tw, Wt[:ns], wg)   # untimed prep
-    ms = min(mt, 256)
-    t0 = time.perf_counter()
-    gemm.w4a4_gemm(L.fmt, ca[:ms], sa[:ms], cw, sw, g, wg)
-    t_g0 = time.perf_counter() - t0
-    reps = int(max(1, min(50, 0.5 * target_s / max(t_g0, 1e-9))))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        gemm.w4a4_gemm(L.fmt, ca[:ms], sa[:ms], cw, sw, g, wg)
-    t_g = (time.perf_counter() - t0) / reps
-    per_flop = t_g / (2.0 * ms * ns * L.K)
-    step_s = (t_tq / mt) * L.M + per_flop * L.gemm_flops()
+                def tq(T, rows, gg):
+                    return quant.transform_quant(fmt, T, rows, g=gg, identity=ident)
+
+                def apply(T, rows):
+                    return quant.apply_transform(T, rows, identity=ident)
+        # size the sample from a short pooled run: about half the target per layer for this leg
+        cal = min(M, 32 * workers)
+        gx = quant.nvfp4_tensor_scale(apply(Tx, X[:cal])) if fmt == "nvfp4" else None
+        t0 = time.perf_counter()
+        _oracle_tq_pool(tq, Tx, X[:cal], gx, workers)
+        per_row = (time.perf_counter() - t0) / cal
+        budget = 0.5 * target_s / len(cases)
+        mt = int(max(cal, min(M, budget / max(per_row, 1e-9))))
+        if fmt == "nvfp4":   # the oracle's own tensor scale of the sample (untimed)
+            gx = quant.nvfp4_tensor_scale(apply(Tx, X[:mt]))
+        t0 = time.perf_counter()
+        ca, sa = _oracle_tq_pool(tq, Tx, X[:mt], gx, workers)
+        t_tq = time.perf_counter() - t0
+        ns = min(N, 1024)
+        gw = quant.nvfp4_tensor_scale(apply(Tw, Wt[:ns])) if fmt == "nvfp4" else None
+        cw, sw = _oracle_tq_pool(tq, Tw, Wt[:ns], gw, workers)     # untimed prep
+        ms = min(mt, 256)
+        with threadpool_limits(workers):
+            t0 = time.perf_counter()
+            gemm.w4a4_gemm(fmt, ca[:ms], sa[:ms], cw, sw, gx, gw)
+            t_g0 = time.perf_counter() - t0
+            reps = int(max(1, min(50, 0.5 * budget / max(t_g0, 1e-9))))
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                gemm.w4a4_gemm(fmt, ca[:ms], sa[:ms], cw, sw, gx, gw)
+            t_g = (time.perf_counter() - t0) / reps
+        layer_flops = 2.0 * M * N * K
+        layer_s = (t_tq / mt) * M + t_g / (2.0 * ms * ns * K) * layer_flops
+        step_s += layer_s
+        flops += layer_flops
+        notes.append(f"{wl.name}: transform+quantize of {mt} of {M} tokens over {workers} processes "
+                     f"({t_tq:.1f} s wall); decode+fp64 matmul of {ms} tokens x {ns} weight rows x K={K} "
+                     f"({reps} reps, {t_g:.3f} s each, {workers} BLAS threads); scaled to the layer "
+                     f"({layer_s:.0f} s)")
     return {
-        "value": L.gemm_flops() / step_s / 1e12,
+        "value": flops / step_s / 1e12,
         "unit": "TFLOP/s",
-        "cores": cpu_threads(),
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"transform+quantize of {mt} of {L.M} tokens ({t_tq:.1f} s); decode+fp64 matmul of "
-                   f"{ms} tokens x {ns} weight rows x K={L.K} ({reps} reps, {t_g:.2f} s each); "
-                   f"scaled to the full {L.M}x{L.N}x{L.K} step ({step_s:.0f} s)"),
+        "sample": "; ".join(notes) + f"; whole step {step_s:.0f} s",
         "host_cpus": os.cpu_count(),
     }
 
@@ -340,8 +402,23 @@ def main():
         sys.exit(2)
 
     import torch
+    from synth.gen import CONFIGS, make_weights, make_activations
+
+    layer_workload = args.workload not in ("had256", "moments", "build", "mfma_ceiling") and not args.copy_reference
+    if layer_workload:
+        if args.workload == "qwen3_14b":
+            wls = [CONFIGS["qwen3_14b_up"], CONFIGS["qwen3_14b_down"]]
+        else:
+            wls = [CONFIGS[args.workload]]
+        fmt = args.fmt or wls[0].formats[0]
+        kind = args.kind or ("wush" if "wush" in wls[0].kinds else wls[0].kinds[-1])
+        cases = [(wl, make_weights(wl), make_activations(wl)) for wl in wls]
+        # the oracle's timing forks worker processes, so it runs before anything touches the GPU
+        cpu = None
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(cases, fmt, kind, args.shared, args.cpu_seconds, host_workers(args.cpu_workers))
+
     import aware_block_transforms_amd as W
-    from synth.gen import CONFIGS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -363,15 +440,12 @@ def main():
         return bench_moments(args, W, torch)
     if args.workload == "build":
         return bench_build(args, W, torch)
+    if args.workload == "mfma_ceiling":
+        return bench_mfma_ceiling(args, torch)
 
-    if args.workload == "qwen3_14b":
-        wls = [CONFIGS["qwen3_14b_up"], CONFIGS["qwen3_14b_down"]]
-    else:
-        wls = [CONFIGS[args.workload]]
-    fmt = args.fmt or wls[0].formats[0]
-    kind = args.kind or ("wush" if "wush" in wls[0].kinds else wls[0].kinds[-1])
-    layers = [Layer(wl, fmt, kind, args.rotate, W, torch, shared=args.shared, planes=not args.row_major_scales)
-              for wl in wls]
+    layers = [Layer(wl, fmt, kind, args.rotate, W, torch, Wt, X, shared=args.shared,
+                    planes=not args.row_major_scales) for wl, Wt, X in cases]
+    del cases
 
     ms_step, tq_ms, gm_ms = run_layer_steps(layers, W, torch, args.steps, args.warmup, args.rotate)
 
@@ -391,7 +465,7 @@ def main():
     gemm_name = "wush_w4a4_gemm_mx_planes" if layers[0].planes else "wush_w4a4_gemm"
     roof_gemm = {"kernel": gemm_name, "bound": "mfma", "achieved": round(gemm_achieved, 2),
                  "peak": gemm_peak, "unit": "TFLOP/s", "frac": round(gemm_achieved / gemm_peak, 4),
-                 "traffic": measured_traffic(gemm_name, wname) if fmt == "mxfp4" else None,
+                 "traffic": measured_traffic(gemm_name, [L.wl.name for L in layers]) if fmt == "mxfp4" else None,
                  "algorithmic_bytes": round(sum(L.gemm_bytes() for L in layers) / len(layers)),
                  "avg_us": round(gm_t * 1e6 / len(layers), 2)}
     if fmt == "int4":
@@ -403,21 +477,31 @@ def main():
     tq_name = ("wush_transform_quant_hd" if layers[0].hd else
                "wush_transform_quant_shared" if layers[0].group is not None else
                "wush_transform_quant_mx_planes" if layers[0].planes else "wush_transform_quant")
-    # dense transforms: fp32 matrix cores; the diagonal variant: vector ALU
-    tq_peak, tq_bound = (VALU_FP32_TFLOPS, "alu") if layers[0].hd else (MFMA_FP32_TFLOPS, "mfma")
-    t_alu = tq_flops / (tq_peak * 1e12)
+    # Each layer's transform+quantize is priced on the engine its kernel runs on
+    # (tq_engine) and on HBM; the step's bound is the slower of the two summed
+    # over layers.
+    engines = [tq_engine(L) for L in layers]
+    t_alu = sum(L.tq_flops() / (peak * 1e12) for L, (_, peak) in zip(layers, engines))
     t_hbm = tq_bytes / (HBM_GBPS * 1e9)
+    tq_bound, tq_peak = engines[0]
+    lnames = [L.wl.name for L in layers]
     if t_alu > t_hbm:
         roof_tq = {"kernel": tq_name, "bound": tq_bound, "achieved": round(tq_alu, 2),
-                   "peak": round(tq_peak, 1), "unit": "TFLOP/s", "frac": round(tq_alu / tq_peak, 4),
-                   "traffic": measured_traffic(tq_name, wname) if fmt == "mxfp4" else None,
+                   "peak": round(tq_peak, 1), "unit": "TFLOP/s", "frac": round(t_alu / tq_t, 4),
+                   "traffic": measured_traffic(tq_name, lnames) if fmt == "mxfp4" else None,
                    "algorithmic_bytes": round(tq_bytes / len(layers)), "avg_us": round(tq_t * 1e6 / len(layers), 2),
                    "hbm_GBps": round(tq_gbps, 1), "hbm_frac": round(tq_gbps / HBM_GBPS, 4)}
     else:
         roof_tq = {"kernel": tq_name, "bound": "hbm", "achieved": round(tq_gbps, 1),
                    "peak": HBM_GBPS, "unit": "GB/s", "frac": round(tq_gbps / HBM_GBPS, 4),
-                   "traffic": measured_traffic(tq_name, wname) if fmt == "mxfp4" else None,
-                   "algorithmic_bytes": round(tq_bytes / len(layers)), "avg_us": round(tq_t * 1e6 / len(layers), 2)}
+                   "traffic": measured_traffic(tq_name, lnames) if fmt == "mxfp4" else None,
+                   "algorithmic_bytes": round(tq_bytes / len(layers)), "avg_us": round(tq_t * 1e6 / len(layers), 2),
+                   **({"engine": tq_bound, "engine_frac": round(t_alu / tq_t, 4)} if t_alu > 0 else {})}
+    if len(layers) > 1:
+        roof_tq["per_layer_us"] = [round(t * 1e3, 2) for t in tq_ms]
+        roof_gemm["per_layer_us"] = [round(t * 1e3, 2) for t in gm_ms]
+        roof_gemm["per_layer_frac"] = [round(L.gemm_flops() / (t / 1e3) / 1e12 / gemm_peak, 4)
+                                       for L, t in zip(layers, gm_ms)]
     out = {
         "metric": METRIC,
         "value": round(flops / (ms_step / 1e3) / 1e12, 2),
@@ -443,8 +527,8 @@ def main():
         "tq_roofline": roof_tq,
         "gemm_roofline": roof_gemm,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
@@ -488,7 +572,7 @@ def bench_had256(args, W, torch):
            "tflops": round(flops / (ms / 1e3) / 1e12, 3),
            "roofline": {"kernel": "wush_had256_gemv", "bound": "hbm", "achieved": round(gbps, 1),
                         "peak": HBM_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_GBPS, 4),
-                        "traffic": measured_traffic("wush_had256_gemv_b%d" % B, wl.name),
+                        "traffic": measured_traffic("wush_had256_gemv_b%d" % B, [wl.name]),
                         "avg_us": round(ms * 1e3, 2)}}
     print(json.dumps(out), flush=True)
 
@@ -567,6 +651,72 @@ def bench_build(args, W, torch):
                         "peak": FP64_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP64_TFLOPS, 5),
                         "traffic": None, "avg_us": round(ms * 1e3, 1)}}
     print(json.dumps(out), flush=True)
+
+
+def bench_mfma_ceiling(args, torch):
+    """Matrix-core rates with operands in registers (libwush_ceiling.so).
+
+    FP4 block-scaled MFMA streams (the W4A4 matmul's instruction) on random and
+    on zero operand bits, one wave per SIMD; fp32 16x16x4 MFMA (the dense
+    transform's instruction) as 2 or 8 accumulation chains of 8 steps, at one
+    and four waves per SIMD, alone and with independent vector FMAs between the
+    MFMAs, plus the vector FMAs alone.  The value is the random-operand FP4
+    rate of the 16x16x128 instruction.
+    """
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "aware_block_transforms_amd", "libwush_ceiling.so"))
+    lib.wush_ceiling_fp4.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
+    lib.wush_ceiling_f32.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    rng = np.random.default_rng([7, 7])
+    rand_bits = torch.from_numpy(rng.integers(0, 2**32, 1024 * 16, dtype=np.uint64).astype(np.uint32).view(np.int32)).cuda()
+    zero_bits = torch.zeros(1024 * 16, dtype=torch.int32, device="cuda")
+    f32_src = torch.from_numpy(rng.standard_normal(1024 * 16).astype(np.float32)).cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 4 * 256, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 1e3
+            best = t if best is None else min(best, t)
+        return best
+
+    res = {}
+    it4 = 4000
+    for which, name, per_instr, nacc in ((0, "16x16x128", 16 * 16 * 128 * 2, 8), (1, "32x32x64", 32 * 32 * 64 * 2, 4)):
+        for label, bits in (("random", rand_bits), ("zero", zero_bits)):
+            def run(w=which, b=bits):
+                assert lib.wush_ceiling_fp4(w, cus, it4, b.data_ptr(), out.data_ptr(), sp) == 0
+            t = timed(run)
+            res[f"fp4_{name}_{label}_TFLOPs"] = round(cus * 4 * it4 * nacc * per_instr / t / 1e12, 1)
+    it32 = 4000
+    for wps in (1, 4):
+        for nchain, nvalu in ((2, 0), (8, 0), (2, 4), (2, 8), (8, 8), (0, 8)):
+            def run(c=nchain, v=nvalu, w=wps):
+                assert lib.wush_ceiling_f32(c, v, cus * w, it32, f32_src.data_ptr(), out.data_ptr(), sp) == 0
+            t = timed(run)
+            key = f"f32_{wps}w_chains{nchain}_valu{nvalu}"
+            res[key + "_us"] = round(t * 1e6, 1)
+            if nchain:
+                res[key + "_TFLOPs"] = round(cus * 4 * wps * it32 * nchain * 8 * 2048 / t / 1e12, 1)
+    v = res["fp4_16x16x128_random_TFLOPs"]
+    print(json.dumps({"metric": "matrix-core ceiling, operands in registers", "value": v, "unit": "TFLOP/s",
+                      "n_gpus": 1, "steps": 5, "warmup": 1, "ms_per_step": None, "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
+                      "config": {"workload": "mfma-ceiling", "cus": cus},
+                      "roofline": {"kernel": "fp4_stream 16x16x128", "bound": "mfma", "achieved": v,
+                                   "peak": MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(v / MXFP4_TFLOPS, 4),
+                                   "traffic": None},
+                      "rates": res}), flush=True)
 
 
 if __name__ == "__main__":
