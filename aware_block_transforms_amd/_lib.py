@@ -63,6 +63,8 @@ _SIGS = {
     "wush_pack_weights_hd": ([_i, _i, _i, _p, _p, _p, _p, _fp, _p], _i),
     "wush_w4a4_gemm_ws_bytes": ([_i, _i, _i, _i], _sz),
     "wush_w4a4_gemm": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _f, _p, _p, _sz, _p], _i),
+    "wush_w4a4_gemm_noalloc_max_ws_bytes": ([], _sz),
+    "wush_w4a4_gemm_noalloc": ([_i, _i, _i, _i, _p, _p, _f, _p, _p, _f, _p, _p], _i),
     "wush_layer_loss": ([_i, _i, _p, _p, _p, _p, _p], _i),
     "wush_loss_ws_bytes": ([_i, _i], _sz),
     "wush_had256_packed_bytes": ([_i, _i], _sz),
@@ -333,6 +335,17 @@ def wush_w4a4_gemm(fmt, a_codes, a_scales, b_codes, b_scales, Y, a_g=1.0, b_g=1.
     wp, wb = _ws(ws)
     _check(lib.wush_w4a4_gemm(_fmt(fmt), M, N, K, _ptr(a_codes), _ptr(a_scales), float(a_g), _ptr(b_codes),
                               _ptr(b_scales), float(b_g), _ptr(Y), wp, wb, _stream(stream)), "wush_w4a4_gemm")
+
+
+def wush_w4a4_gemm_noalloc_max_ws_bytes():
+    return lib.wush_w4a4_gemm_noalloc_max_ws_bytes()
+
+
+def wush_w4a4_gemm_noalloc(fmt, a_codes, a_scales, b_codes, b_scales, Y, a_g=1.0, b_g=1.0, stream=None):
+    M, N = Y.shape
+    K = a_codes.shape[1] * 2
+    _check(lib.wush_w4a4_gemm_noalloc(_fmt(fmt), M, N, K, _ptr(a_codes), _ptr(a_scales), float(a_g), _ptr(b_codes),
+                                      _ptr(b_scales), float(b_g), _ptr(Y), _stream(stream)), "wush_w4a4_gemm_noalloc")
 
 
 def wush_loss_ws_bytes(M, N):

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 
@@ -84,4 +85,67 @@ extern "C" wush_status wush_w4a4_gemm_mx_planes(int M, int N, int K, const uint8
       !wush::aligned16(b_planes))
     return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm_mx_planes: codes, planes and Y must be 16-byte aligned");
   return wush::gemm_mxfp4_planes(M, N, K, a_codes, a_planes, b_codes, b_planes, Y, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// wush_w4a4_gemm_noalloc: the same matmul for callers that cannot allocate
+// (code under graph capture, serving loops, harnesses that forbid hipMalloc).
+// The scale re-layout goes to a fixed device array instead of a workspace.  In
+// host code `scratch` names a host-side stand-in, not device memory, so the
+// kernels only ever see the address hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.  Every call on a device shares
+// that device's array; its pre-passes rewrite every byte the kernels read, so
+// nothing needs clearing, and calls that overlap on one device race.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];   // device address of `scratch` per device, once looked up
+
+wush_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "wush_w4a4_gemm_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return wush::fail(WUSH_E_HIP, "wush_w4a4_gemm_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return wush::fail(WUSH_E_HIP, "wush_w4a4_gemm_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    scratch_dev[dev] = ptr;
+  }
+  *out = scratch_dev[dev];
+  return WUSH_OK;
+}
+
+}  // namespace
+
+extern "C" size_t wush_w4a4_gemm_noalloc_max_ws_bytes(void) { return kScratchBytes; }
+
+extern "C" wush_status wush_w4a4_gemm_noalloc(wush_format fmt, int M, int N, int K, const uint8_t* a_codes,
+                                              const void* a_scales, float a_g, const uint8_t* b_codes,
+                                              const void* b_scales, float b_g, float* Y, void* stream) {
+  if (wush_format_block(fmt) == 0)
+    return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm_noalloc: bad format %d", static_cast<int>(fmt));
+  if (M < 1 || N < 1 || K < 128 || K % 128)
+    return wush::fail(WUSH_E_SHAPE,
+                      "wush_w4a4_gemm_noalloc: need M, N >= 1 and K a positive multiple of 128 (M=%d N=%d K=%d)", M, N,
+                      K);
+  const size_t need = wush_w4a4_gemm_ws_bytes(fmt, M, N, K);
+  if (need > kScratchBytes)
+    return wush::fail(WUSH_E_SHAPE,
+                      "wush_w4a4_gemm_noalloc: M=%d N=%d K=%d needs %zu bytes of scratch, above the fixed %zu",
+                      M, N, K, need, kScratchBytes);
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !Y)
+    return wush::fail(WUSH_E_ARG, "wush_w4a4_gemm_noalloc: null pointer");
+  void* ws = nullptr;
+  const wush_status st = scratch_for_current_device(&ws);
+  if (st != WUSH_OK) return st;
+  // never NULL here, so the general call cannot fall back to the memory pool
+  return wush_w4a4_gemm(fmt, M, N, K, a_codes, a_scales, a_g, b_codes, b_scales, b_g, Y, ws, kScratchBytes, stream);
 }

@@ -318,6 +318,24 @@ wush_status wush_w4a4_gemm(wush_format fmt, int M, int N, int K,
                            const uint8_t* b_codes, const void* b_scales, float b_g,
                            float* Y, void* ws, size_t ws_bytes, void* stream);
 
+/* wush_w4a4_gemm without allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, result and errors as wush_w4a4_gemm
+ * except ws: the scale re-layout goes to a fixed 16 MiB device array that the
+ * library holds on every device it runs on until the process ends
+ * (wush_w4a4_gemm_noalloc_max_ws_bytes()).  Shapes whose
+ * wush_w4a4_gemm_ws_bytes exceed it return WUSH_E_SHAPE before anything is
+ * launched (MXFP4 fits both Qwen3-14B MLP projections at 16384 tokens; NVFP4
+ * and INT4 fit the 4096 x 4096 x 8192-token square).  Calls no hipMalloc or
+ * hipFree.  All calls on one device share its array: calls that overlap on
+ * that device (two streams, two threads) race and must be ordered by the
+ * caller.  The stream must belong to the current device. */
+size_t wush_w4a4_gemm_noalloc_max_ws_bytes(void);
+wush_status wush_w4a4_gemm_noalloc(wush_format fmt, int M, int N, int K,
+                                   const uint8_t* a_codes, const void* a_scales, float a_g,
+                                   const uint8_t* b_codes, const void* b_scales, float b_g,
+                                   float* Y, void* stream);
+
 /* Layer loss of [WUSH-radio] "Problem Setup and Goal":
  *   *loss = sum over M x N of (Yhat - Yref)^2 / (M * N), accumulated in fp64
  *   with a fixed two-stage reduction order (deterministic).
