@@ -293,3 +293,123 @@ def test_block_moments_dev_checks_and_workspace_size():
     assert L.wush_block_moments_dev(24, 0, 10, 96, None, None, None, 0, None) == W.WUSH_E_SHAPE
     assert L.wush_block_moments_dev(32, 0, 0, 64, None, None, None, 0, None) == W.WUSH_E_SHAPE
     assert L.wush_block_moments_dev(32, 0, 10, 64, None, None, None, 0, None) == W.WUSH_E_ARG
+
+
+def _device_asm(src):
+    import subprocess
+    from aware_block_transforms_amd import build as B
+    r = subprocess.run([B.HIPCC, *B.HIP_FLAGS, *B.HIP_EXTRA.get(src, []), "--cuda-device-only", "-S", "-o", "-",
+                        os.path.join(B.CSRC, src)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return r.stdout
+
+
+def _kernel_code(asm, name):
+    """Instructions (and labels) of the kernel whose symbol contains `name`."""
+    import re
+    out, on = [], False
+    for line in asm.splitlines():
+        if not on and re.match(r"^_Z\S*:", line) and name in line.split(":")[0]:
+            on = True
+            continue
+        if on:
+            t = line.split(";")[0].strip()
+            if t.startswith("s_endpgm"):
+                break
+            if not t or t.startswith((".", "//")) and not re.match(r"^\.LBB\w*:", t):
+                continue
+            out.append(t)
+    return out
+
+
+def _vregs(tok):
+    """VGPR numbers named by an operand token: v7 -> {7}, v[4:7] -> {4..7}."""
+    import re
+    m = re.fullmatch(r"v(\d+)", tok)
+    if m:
+        return {int(m.group(1))}
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    return set()
+
+
+def _asm_mfma_hazards(code, gap=3, acc_wait=19):
+    """Hazards of inline-asm MFMAs in compiled code (list of instructions and labels).
+
+    Returns the violations: a vector-ALU instruction writing an MFMA's A or B
+    operand with fewer than `gap` wait states between it and the MFMA (s_nop N counts N + 1; branches
+    into a label are followed back to their source, so a loop's back edge is
+    covered), and fewer than `acc_wait` wait states between the last MFMA and
+    the first instruction that reads an AGPR.
+    """
+    import re
+    preds = {}
+    for i, l in enumerate(code):
+        m = re.match(r"s_c?branch\w*\s+(\.LBB\w+)", l)
+        if m:
+            preds.setdefault(m.group(1), []).append(i)
+
+    def wait_states(ins):
+        m = re.match(r"s_nop\s+(\d+)", ins)
+        return int(m.group(1)) + 1 if m else 1
+
+    def before(i, need, seen):
+        found, k, left = [], i - 1, need
+        while left > 0 and k >= 0:
+            ins = code[k]
+            if ins.endswith(":"):
+                for b in preds.get(ins[:-1], []):
+                    if (b, left) not in seen:
+                        seen.add((b, left))
+                        found += before(b + 1, left, seen)
+                k -= 1
+                continue
+            found.append(ins)
+            left -= wait_states(ins)
+            k -= 1
+        return found
+
+    bad = []
+    mfmas = [i for i, l in enumerate(code) if l.startswith("v_mfma")]
+    for i in mfmas:
+        ops = [t.strip() for t in code[i].split(None, 1)[1].split(",")]
+        srcs = _vregs(ops[1]) | _vregs(ops[2])
+        for prev in before(i, gap, set()):
+            if prev.startswith("v_") and not prev.startswith("v_mfma") and " " in prev:
+                if _vregs(prev.split(None, 1)[1].split(",")[0].strip()) & srcs:
+                    bad.append((code[i], prev))
+    if mfmas:
+        ws = 0
+        for ins in code[mfmas[-1] + 1:]:
+            if not ins.endswith(":") and re.search(r"\ba(\d+|\[\d+:\d+\])", ins.split(None, 1)[-1]):
+                break
+            ws += 0 if ins.endswith(":") else wait_states(ins)
+        if ws < acc_wait:
+            bad.append(("accumulators read after", ws))
+    return bad
+
+
+def test_asm_mfma_hazard_checker_on_planted_cases():
+    mfma = "v_mfma_f32_32x32x16_f16 a[0:15], v[4:7], v[8:11], a[0:15]"
+    tail = ["s_nop 15", "s_nop 3", "v_accvgpr_read_b32 v0, a0"]
+    assert _asm_mfma_hazards(["v_mov_b32_e32 v5, 0", mfma] + tail)                  # no wait state between
+    assert _asm_mfma_hazards(["v_mov_b32_e32 v9, 0", "s_nop 1", mfma] + tail)       # 2 wait states between
+    assert not _asm_mfma_hazards(["v_mov_b32_e32 v9, 0", "s_nop 2", mfma] + tail)   # 3 wait states between
+    assert not _asm_mfma_hazards(["v_mov_b32_e32 v12, 0", mfma] + tail)             # not an operand
+    # written at the end of the loop body, read by the MFMA at the loop head
+    loop = [".LBB0_1:", mfma, "s_nop 7", "v_mov_b32_e32 v6, 1", "s_cbranch_scc1 .LBB0_1"] + tail
+    assert _asm_mfma_hazards(loop)
+    # accumulators read too early
+    assert _asm_mfma_hazards(["s_nop 7", mfma, "s_nop 3", "v_accvgpr_read_b32 v0, a0"])
+
+
+def test_asm_mfma_operands_are_written_early():
+    """The NVFP4 matmul issues its MFMAs as inline asm, which the compiler's
+    hazard recognizer does not see.  In the compiled kernel no vector-ALU
+    instruction may write an MFMA's A or B operand with fewer than three wait
+    states between the write and the MFMA, and the accumulators are read only after at least 19
+    wait states past the last MFMA (see _asm_mfma_hazards)."""
+    code = _kernel_code(_device_asm("gemm_nvfp4.hip"), "gemm_nvfp4_lds")
+    assert sum(1 for l in code if l.startswith("v_mfma")) >= 64
+    assert _asm_mfma_hazards(code) == []
