@@ -7,23 +7,24 @@
 // "WUSH: Near-Optimal Adaptive Transforms for LLM Quantization" (AI Radio),
 // "The gist": transform and quantizer run as one fused GPU kernel.
 //
-// Work mapping (CDNA4, wave64):
-//  * one wave owns one block b of channels and two tiles of 64 tokens; lane
-//    l holds tokens base + l and base + 64 + l.  The block's bs x bs matrix is
-//    identical for every lane, so it is read with scalar loads into SGPRs and
-//    broadcast to the FMAs for free, each element serving both tokens (the
-//    scalar cache's bandwidth, not the VALU, bounds a one-token loop); the
-//    wave's x values stay in VGPRs.
-//  * y_i = fma chain over k (ascending, from +0) in fp32: bs*bs v_fma_f32 per
-//    lane and block.  All bs outputs of a block live in one lane, so the block
-//    maximum needs no cross-lane reduction.
-//  * the lane packs its bs codes into bs/2 contiguous bytes (one 16-byte store
-//    at bs = 32) and stores one scale.
+// Kernels:
+//  * tq_dense_kernel: every non-identity block matrix, bf16 or fp32 x, all
+//    formats, the unquantized values (wush_transform_apply) and the NVFP4
+//    tensor maximum.  The transform runs on the fp32 matrix cores as a chain of
+//    v_mfma_f32_16x16x4_f32, which reproduces the pinned FMA chain bit for bit;
+//    each wave streams 16-token units of two adjacent 32-channel spans with the
+//    next units' loads in flight, transposes x across its lane groups with lane
+//    swaps (no LDS), and encodes with the pinned block quantizers.
+//  * tq_ident_kernel: the identity transform (a bit-exact copy), one block per
+//    lane.
+//  * tq_hd_kernel: the Hadamard-diagonal variant, one product and log2(bs)
+//    butterfly stages per element on the vector ALU.
 // The arithmetic is pinned (see wush.h): codes and scales are bit-exact
 // functions of (T, x).
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "common.h"
@@ -34,7 +35,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;
-constexpr int kTokensPerWave = 2 * kWave;   // two 64-token tiles per wave
+constexpr int kTokensPerWave = 2 * kWave;   // identity kernel: two 64-token tiles per wave
 
 // kApply: write y itself (fp32); kMXP: MXFP4 with the scales written in the
 // plane order of the MXFP4 matmul's LDS stage (see mxfp4_plane_offset)
@@ -96,50 +97,19 @@ __device__ __forceinline__ void load_block(const void* __restrict__ X, size_t of
   }
 }
 
-// y = T x for two tokens at once, each with the pinned fp32 FMA chain.  Tb is
-// wave-uniform (scalar loads into SGPRs); every T element fetched through the
-// scalar cache feeds two FMAs, which halves the scalar-cache traffic that
-// otherwise bounds this kernel.
-// Rows of T are double-buffered in SGPRs: row i+1 is requested before the
-// FMAs of row i, and the fences keep the compiler from hoisting every row's
-// loads (which runs out of SGPRs and spills them to VGPR lanes).
-template <int BS>
-__device__ __forceinline__ void transform2(const float* __restrict__ Tb, const float (&x0)[BS], const float (&x1)[BS],
-                                           float (&y0)[BS], float (&y1)[BS]) {
-  float tc[BS], tn[BS];
-#pragma unroll
-  for (int k = 0; k < BS; ++k) tc[k] = Tb[k];
-#pragma unroll
-  for (int i = 0; i < BS; ++i) {
-    if (i + 1 < BS) {
-#pragma unroll
-      for (int k = 0; k < BS; ++k) tn[k] = Tb[(i + 1) * BS + k];
-    }
-    float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < BS; ++k) {
-      a0 = __builtin_fmaf(tc[k], x0[k], a0);
-      a1 = __builtin_fmaf(tc[k], x1[k], a1);
-    }
-    y0[i] = a0;
-    y1[i] = a1;
-#pragma unroll
-    for (int k = 0; k < BS; ++k) tc[k] = tn[k];
-    asm volatile("" ::: "memory");   // keeps the next row's loads here at the IR level too
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // Two E2M1 codes into byte `sel` of `old` (low nibble = a).  gfx950's packed FP4
 // conversion rounds to nearest with ties to the even code, saturates at 6 and keeps
-// the sign bit, which is exactly the pinned encoder for every non-NaN input; the
-// scale operand divides, so 1.0 leaves the values unchanged.
-__device__ __forceinline__ uint32_t cvt_pair(uint32_t old, float a, float b, int sel) {
+// the sign bit, which is exactly the pinned encoder for every non-NaN input.  Its
+// scale operand s divides the values by the power of two that s's exponent field
+// encodes, as an E8M0 byte (field 0 meaning 2^-127; checked on the GPU over zero,
+// subnormal, tie and saturating blocks): s = 1.0 leaves them unchanged, and for
+// MXFP4 s = the block scale 2^e replaces the multiplication by 2^-e.
+__device__ __forceinline__ uint32_t cvt_pair_s(uint32_t old, float a, float b, float s, int sel) {
   switch (sel) {
-    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0);
-    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
-    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 2);
-    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 3);
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, s, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, s, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, s, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, s, 3);
   }
 }
 
@@ -158,6 +128,7 @@ __device__ __forceinline__ void store_codes(uint8_t* __restrict__ dst, const uin
 template <int FMT>
 struct BlockQuant {
   float mul;        // multiplier applied to each value before encoding
+  float div;        // MXFP4: the scale 2^e, applied by the conversion itself
   uint32_t scale;   // scale byte (E8M0, E4M3) or fp16 bits (INT4)
   bool zero;        // codes forced to 0
   bool soft;        // NVFP4 with 1/s not finite: the software encoder (0 * inf is NaN -> code 0)
@@ -165,12 +136,13 @@ struct BlockQuant {
 
 template <int FMT>
 __device__ __forceinline__ BlockQuant<FMT> block_quant(uint32_t ab, float g) {
-  BlockQuant<FMT> q{1.0f, 0u, false, false};
+  BlockQuant<FMT> q{1.0f, 1.0f, 0u, false, false};
   const bool bad = ab >= 0x7f800000u;          // NaN or Inf in the block
   if constexpr (FMT == kMX) {
     const uint32_t ex = ab >> 23;
     const uint32_t sbyte = ex > 2u ? ex - 2u : 0u;             // e + 127
     q.mul = __uint_as_float((254u - sbyte) << 23);             // 2^-e
+    q.div = __uint_as_float(sbyte << 23);                      // 2^e, the E8M0 byte as exponent field
     q.zero = bad;
     q.scale = bad ? 0xffu : sbyte;
   } else if constexpr (FMT == kNV) {
@@ -215,7 +187,12 @@ __device__ __forceinline__ void encode_pairs(const float (&y)[2 * NP], const Blo
     if constexpr (FMT == kNV) soft = q.soft;
     if (!soft) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) w[p >> 2] = cvt_pair(w[p >> 2], y[2 * p] * q.mul, y[2 * p + 1] * q.mul, p & 3);
+      for (int p = 0; p < NP; ++p) {
+        if constexpr (FMT == kMX)
+          w[p >> 2] = cvt_pair_s(w[p >> 2], y[2 * p], y[2 * p + 1], q.div, p & 3);
+        else
+          w[p >> 2] = cvt_pair_s(w[p >> 2], y[2 * p] * q.mul, y[2 * p + 1] * q.mul, 1.0f, p & 3);
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < 2 * NP; ++k) w[k >> 3] |= e2m1_code_nan0(y[k] * q.mul) << (4 * (k & 7));
@@ -268,50 +245,32 @@ __device__ __forceinline__ void encode_store(const float (&y)[BS], size_t row, i
   }
 }
 
-// One kernel for the three formats plus an amax-only pass (NVFP4 tensor scale).
-// A wave owns one block and two 64-token tiles: lane l transforms tokens
-// base + l and base + 64 + l together (see transform2).
-template <int BS, int FMT, bool BF16, bool IDENT>
-__global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves_per_eu(4))) void tq_kernel(
-    const void* __restrict__ X, const float* __restrict__ T, int n, int d_in, float g,
-    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out,
-    const int* __restrict__ tmap, int ngroups) {
+// Identity transform (a bit-exact copy) with the three formats plus an
+// amax-only pass (NVFP4 tensor scale).  A wave owns one block and two 64-token
+// tiles: lane l quantizes tokens base + l and base + 64 + l, each block's
+// values in one lane, so the block maximum needs no cross-lane reduction (an
+// integer max of |y| bit patterns, which also flags NaN and Inf).
+template <int BS, int FMT, bool BF16>
+__global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves_per_eu(4))) void tq_ident_kernel(
+    const void* __restrict__ X, int n, int d_in, float g, uint8_t* __restrict__ codes, void* __restrict__ scales,
+    uint32_t* __restrict__ amax_out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = d_in / BS;
   const int blk = blockIdx.x * kWavesPerGroup + wave;
   if (blk >= nblk) return;                       // wave-uniform
-  // the block's matrix, or with a group map its group's (ids clamped to the table)
-  const int tsel = tmap ? min(max(tmap[blk], 0), ngroups - 1) : blk;
-  const float* __restrict__ Tb = IDENT ? nullptr : T + static_cast<size_t>(tsel) * BS * BS;
   const int tok0 = blockIdx.y * (2 * kWave) + lane, tok1 = tok0 + kWave;
-  const bool v0 = tok0 < n, v1 = tok1 < n;
   uint32_t run_max = 0;
-
   float x0[BS], x1[BS];
   const size_t col = static_cast<size_t>(blk) * BS;
-  if (v0) load_block<BS, BF16>(X, static_cast<size_t>(tok0) * d_in + col, x0);
-  if (v1) load_block<BS, BF16>(X, static_cast<size_t>(tok1) * d_in + col, x1);
-  else {
-#pragma unroll
-    for (int k = 0; k < BS; ++k) x1[k] = 0.0f;
+  if (tok0 < n) {
+    load_block<BS, BF16>(X, static_cast<size_t>(tok0) * d_in + col, x0);
+    encode_store<BS, FMT>(x0, static_cast<size_t>(tok0), blk, nblk, d_in, g, codes, scales, run_max);
   }
-
-  float y0[BS], y1[BS];
-  if constexpr (IDENT) {
-#pragma unroll
-    for (int k = 0; k < BS; ++k) { y0[k] = x0[k]; y1[k] = x1[k]; }
-  } else {
-    transform2<BS>(Tb, x0, x1, y0, y1);
-    // materialize both tokens' outputs here: left alone, the compiler sinks
-    // each token's FMAs into its (divergent) store branch, and the T values
-    // both branches share then pile up in SGPRs
-#pragma unroll
-    for (int k = 0; k < BS; ++k) asm volatile("" : "+v"(y0[k]), "+v"(y1[k]));
+  if (tok1 < n) {
+    load_block<BS, BF16>(X, static_cast<size_t>(tok1) * d_in + col, x1);
+    encode_store<BS, FMT>(x1, static_cast<size_t>(tok1), blk, nblk, d_in, g, codes, scales, run_max);
   }
-  if (v0) encode_store<BS, FMT>(y0, static_cast<size_t>(tok0), blk, nblk, d_in, g, codes, scales, run_max);
-  if (v1) encode_store<BS, FMT>(y1, static_cast<size_t>(tok1), blk, nblk, d_in, g, codes, scales, run_max);
-
   if constexpr (FMT == kAmax) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) run_max = max(run_max, static_cast<uint32_t>(__shfl_xor(static_cast<int>(run_max), off)));
@@ -330,254 +289,401 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves
 // sequential fmaf chain, with uniform, wide-exponent, subnormal, bf16-valued
 // and cancelling operands, and found no difference; a model with one rounding
 // per four products differed in 22-74% of them.)  The matrix cores do 64 fp32
-// flop per clock per SIMD, twice the vector FMA rate, and leave the vector ALU
-// to the encoders.
+// flop per clock per SIMD, twice the vector FMA rate.  On this part vector-ALU
+// instructions do not run under an fp32 MFMA (measured: their times add), so
+// the kernel keeps its vector work per token small.
 //
-// Mapping: a wave owns one channel block and a run of tokens.  For one group
-// of 16 tokens, output rows 16h .. 16h+15 of T form the 16 x 16 product
-// T[16h.., :] * X_group^T, computed as bs/4 MFMAs: lane (g = l / 16, j = l % 16)
-// supplies T[16h + j][4c + g] and x[token j][4c + g] to step c and ends with
-// y[token j][16h + 4g + e] in register e.
+// Work unit: 16 tokens x one 32-channel span (one block at bs 32, two at
+// bs 16).  A wave owns kSpans adjacent spans (128 bytes of every bf16 row,
+// the four waves of a workgroup 512 contiguous bytes) and walks a run of
+// units with the loads of the next kDepth units in flight.  Lane
+// (g = l / 16, j = l % 16) works on token j of the unit.
 //
-// The lane therefore needs every fourth element of a row.  Loading that
-// directly (one dword per step, 16 rows per instruction) keeps the texture
-// path busy for most of the kernel, so x is read in coalesced 16-byte pieces
-// (a unit of 512/bs bf16 rows, one piece per lane) and transposed through
-// the wave's own LDS: the piece of elements 8q .. 8q+7 is written as four
-// dwords, dword r pairing elements 8q + r and 8q + 4 + r (one v_perm each),
-// to row t, slot (r, q), so that lane (g, j) then reads its bs/4 elements as
-// bs/8 consecutive dwords (one ds_read_b128 at bs 32).  Row strides of 20
-// (bs 32) and 10 (bs 16) dwords make both sides bank-conflict-free.  T is
-// staged the same way once per wave (row stride bs + 4 dwords) and its
-// fragments kept in bs * bs / 64 VGPRs.  Four units of x are in flight ahead
-// of the one computed.  fp32 x (weight packing) is read directly, one dword
-// per step.
+// x: lane (q, j) loads 16 bytes of its token's span, elements 8q .. 8q+7
+// (fp32: 32 bytes, two loads).  At step c the MFMA wants element 4c + g in
+// lane group g.  After one v_perm per dword (bf16; it pairs elements 8q + r
+// and 8q + 4 + r), group q holds in dword r what group r needs for steps 2q
+// and 2q+1: a 4 x 4 transpose of dwords across the lane groups, two
+// v_permlane32_swap and two v_permlane16_swap, no LDS round trip.
 //
-// The block maximum of token j is reduced over its four lane groups with two
-// lane shuffles, each lane encodes its own outputs, and the code row of token
-// j (16 bytes at bs 32, 8 at bs 16) is gathered into lane j with three more
-// shuffles and stored once.
-constexpr int kMfmaUnits = 8;     // units of x per wave
-constexpr int kMfmaDepth = 4;     // units loaded ahead of the one computed
+// T: at bs 32 the A operand row i of accumulator h is T row
+// 8 (i / 4) + 4 h + i % 4.  Lane group g then ends with outputs 8g .. 8g+7 of
+// its token (acc[0]: 8g .. 8g+3, acc[1]: 8g+4 .. 8g+7), whose four code
+// bytes are contiguous: one dword store, no lane exchange.  At bs 16
+// accumulator h is block h of the span, and lane group g holds outputs
+// 4g .. 4g+3 of each block.  The fragments are loaded once per wave and
+// transposed like fp32 x.
+//
+// Block maximum: over the lane's values, then over its token's four lane
+// groups with two lane swaps; then the pinned block quantizers.
+//
+// Tokens past n re-read row n - 1 and rewrite its bytes unchanged; spans (and
+// at bs 16 blocks) past d_in repeat the last block the same way, so every
+// load and store stays inside the caller's buffers.
+constexpr int kSpans = 2;    // 32-channel spans per wave
+constexpr int kDepth = 4;    // units of x in flight ahead of the one computed
 
-template <int BS, bool BF16>
-struct XUnit {
-  static constexpr int kRows = BF16 ? 512 / BS : 16;            // tokens per unit
-  static constexpr int kGroups = kRows / 16;
-  static constexpr int kRaw = BF16 ? 4 : BS / 4;                 // dwords per lane
-  static constexpr int kStride = BF16 ? BS / 2 + BS / 8 : 0;     // LDS row stride of x in dwords (20, 10)
-  static constexpr int kTStride = BS + 4;                        // LDS row stride of T
-  static constexpr int kLdsDwords = BS * kTStride + kRows * kStride;
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);   // a's lanes 32..63 <-> b's 0..31
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);   // a's odd rows <-> b's even rows
+  a = r[0];
+  b = r[1];
+}
+// 4 x 4 dword transpose across the lane groups (rows of 16 lanes): on entry
+// d[r] of group q is D[q][r]; on exit d[q] of group r is D[q][r].
+__device__ __forceinline__ void transpose4(uint32_t (&d)[4]) {
+  swap32(d[0], d[2]);
+  swap32(d[1], d[3]);
+  swap16(d[0], d[1]);
+  swap16(d[2], d[3]);
+}
+
+// maximum over the four lane groups of a token (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ uint32_t max_groups(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // values of lanes l & ~16, l | 16
+  const uint32_t m = max(r[0], r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(m, m, false, false);   // values of lanes l & ~32, l | 32
+  return max(t[0], t[1]);
+}
+
+// First element of lane group q's eight in its token row, for span sp.
+template <int BS>
+__device__ __forceinline__ int span_col(int sp, int q, int nblk) {
+  if constexpr (BS == 32) return min(sp, nblk - 1) * 32 + 8 * q;
+  return min(2 * sp + (q >> 1), nblk - 1) * 16 + 8 * (q & 1);
+}
+
+template <bool BF16>
+struct XRaw {
+  static constexpr int kDwords = BF16 ? 4 : 8;
 };
 
-// Raw x of one unit starting at token tb (rows past n re-read row n - 1).
-template <int BS, bool BF16>
-__device__ __forceinline__ void load_unit(const void* X, int tb, int n, int d_in, size_t col, int lane,
-                                          uint32_t (&raw)[XUnit<BS, BF16>::kRaw]) {
+// Rows of one unit: the unit (clamped to the last one that holds tokens) and
+// lane j's row within it (clamped to n - 1).  row0 is wave-uniform, so every
+// address below is a uniform 64-bit base plus a 32-bit lane offset.
+struct UnitRows {
+  size_t row0;   // first token of the unit
+  int jj;        // this lane's token, relative to row0
+};
+__device__ __forceinline__ UnitRows unit_rows(int unit, int n, int j) {
+  const int ue = min(unit, (n - 1) >> 4);
+  return UnitRows{static_cast<size_t>(ue) * 16, min(j, n - 1 - ue * 16)};
+}
+
+// Raw x of one span: elements col .. col + 7 of lane row jj of the unit at row0.
+template <bool BF16>
+__device__ __forceinline__ void load_x(const void* X, const UnitRows& ur, int d_in, int col,
+                                       uint32_t (&raw)[XRaw<BF16>::kDwords]) {
+  const uint32_t off = static_cast<uint32_t>(ur.jj * d_in + col);
   if constexpr (BF16) {
-    const int t = lane / (BS / 8), q = lane % (BS / 8);
-    const uint16_t* p =
-        reinterpret_cast<const uint16_t*>(X) + static_cast<size_t>(min(tb + t, n - 1)) * d_in + col + 8 * q;
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(X) + ur.row0 * d_in;
+    const uint4 v = *reinterpret_cast<const uint4*>(base + off);
     raw[0] = v.x; raw[1] = v.y; raw[2] = v.z; raw[3] = v.w;
   } else {
-    const int j = lane & 15, g = lane >> 4;
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(X) + static_cast<size_t>(min(tb + j, n - 1)) * d_in + col + g;
-#pragma unroll
-    for (int c = 0; c < BS / 4; ++c) raw[c] = p[4 * c];
+    const float* base = reinterpret_cast<const float*>(X) + ur.row0 * d_in;
+    const uint4* p = reinterpret_cast<const uint4*>(base + off);
+    const uint4 a = p[0], b = p[1];
+    raw[0] = a.x; raw[1] = a.y; raw[2] = a.z; raw[3] = a.w;
+    raw[4] = b.x; raw[5] = b.y; raw[6] = b.z; raw[7] = b.w;
   }
 }
 
-// bf16 unit: raw pieces -> LDS rows in step order (see above)
-template <int BS>
-__device__ __forceinline__ void stage_unit(uint32_t* lx, int lane, const uint32_t (&raw)[4]) {
-  constexpr int S = XUnit<BS, true>::kStride;
-  const int t = lane / (BS / 8), q = lane % (BS / 8);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    lx[t * S + r * (BS / 8) + q] =
-        __builtin_amdgcn_perm(raw[2 + (r >> 1)], raw[r >> 1], (r & 1) ? 0x07060302u : 0x05040100u);
-}
-
-// x values of group s of the unit for lane (g, j), in step order c = 0 .. bs/4 - 1
-template <int BS, bool BF16>
-__device__ __forceinline__ void group_x(const uint32_t* lx, const uint32_t (&raw)[XUnit<BS, BF16>::kRaw], int s,
-                                        int lane, float (&xv)[BS / 4]) {
+// x operands of the eight MFMA steps of one span for lane (g, j).
+template <bool BF16>
+__device__ __forceinline__ void x_steps(const uint32_t (&raw)[XRaw<BF16>::kDwords], float (&xv)[8]) {
   if constexpr (BF16) {
-    constexpr int S = XUnit<BS, true>::kStride;
-    const int j = lane & 15, g = lane >> 4;
-    const uint32_t* src = lx + (16 * s + j) * S + g * (BS / 8);
-    uint32_t d[BS / 8];
-    if constexpr (BS == 32) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    } else {
-      const uint2 v = *reinterpret_cast<const uint2*>(src);
-      d[0] = v.x; d[1] = v.y;
-    }
+    uint32_t d[4];
 #pragma unroll
-    for (int q = 0; q < BS / 8; ++q) {
+    for (int r = 0; r < 4; ++r)
+      d[r] = __builtin_amdgcn_perm(raw[2 + (r >> 1)], raw[r >> 1], (r & 1) ? 0x07060302u : 0x05040100u);
+    transpose4(d);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
       xv[2 * q] = __uint_as_float(d[q] << 16);
       xv[2 * q + 1] = __uint_as_float(d[q] & 0xffff0000u);
     }
   } else {
+    uint32_t lo[4] = {raw[0], raw[1], raw[2], raw[3]}, hi[4] = {raw[4], raw[5], raw[6], raw[7]};
+    transpose4(lo);
+    transpose4(hi);
 #pragma unroll
-    for (int c = 0; c < BS / 4; ++c) xv[c] = __uint_as_float(raw[c]);
-  }
-}
-
-// Cross-row lane exchange without an LDS round trip: v_permlane16_swap of a
-// value with itself yields, in every lane, the values of lanes l & ~16 and
-// l | 16; v_permlane32_swap those of l & ~32 and l | 32 (checked on the GPU).
-__device__ __forceinline__ uint32_t bitsel(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
-__device__ __forceinline__ uint32_t max_xor16(uint32_t v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return max(r[0], r[1]);
-}
-__device__ __forceinline__ uint32_t max_xor32(uint32_t v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return max(r[0], r[1]);
-}
-__device__ __forceinline__ uint32_t from_xor16(uint32_t v, bool odd_row) {
-  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return bitsel(0u - static_cast<uint32_t>(odd_row), r[0], r[1]);
-}
-
-// One 16-token group: the MFMA chains, then the block maximum, the encoders
-// and the stores of token `tok` into row `row` (tok clamped to n - 1: a row
-// past the end holds the inputs of row n - 1 and so writes its bytes again).
-// Every lane stores, so the stores sit in straight-line code and the
-// compiler's wait counts keep the loads ahead of them in flight (a store in a
-// lane-masked branch makes every later wait assume it was not issued).
-template <int BS, int FMT>
-__device__ __forceinline__ void mfma_group(const float (&ta)[BS / 16][BS / 4], const float (&xv)[BS / 4], int gq,
-                                           int row, int blk, int nblk, int d_in, float g,
-                                           uint8_t* __restrict__ codes, void* __restrict__ scales,
-                                           uint32_t& run_max) {
-  constexpr int H = BS / 16, C = BS / 4;
-  v4f acc[H];
-#pragma unroll
-  for (int h = 0; h < H; ++h) acc[h] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int c = 0; c < C; ++c)
-#pragma unroll
-    for (int h = 0; h < H; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[h][c], xv[c], acc[h], 0, 0, 0);
-  float y[4 * H];
-#pragma unroll
-  for (int h = 0; h < H; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[4 * h + e] = acc[h][e];
-  if constexpr (FMT == kApply) {
-    float* dst = reinterpret_cast<float*>(codes) + static_cast<size_t>(row) * d_in + static_cast<size_t>(blk) * BS +
-                 4 * gq;
-#pragma unroll
-    for (int h = 0; h < H; ++h)
-      *reinterpret_cast<float4*>(dst + 16 * h) = make_float4(y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]);
-    return;
-  }
-  uint32_t ab = 0;
-#pragma unroll
-  for (int k = 0; k < 4 * H; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
-  ab = max_xor32(max_xor16(ab));
-  if constexpr (FMT == kAmax) {
-    run_max = max(run_max, ab);                // rows past n repeat row n - 1
-  } else {
-    constexpr int QF = FMT == kMXP ? kMX : FMT;
-    const BlockQuant<QF> q = block_quant<QF>(ab, g);
-    uint32_t w[1];
-    encode_pairs<QF, 2 * H>(y, q, w);
-    // Lane group g holds code bytes 2g, 2g+1 (outputs 4g .. 4g+3) in its low
-    // half and, at bs 32, bytes 8+2g, 9+2g in its high half.  Groups 2m and
-    // 2m+1 together form dword m of the row (low halves) and, at bs 32,
-    // dword 2 + m (high halves).  Group g stores dword g (bs 32) or g % 2
-    // (bs 16, each dword twice); groups 1 and 2 take theirs from the other pair.
-    // (selections as bit masks: written as conditionals they become branches)
-    const uint32_t m_odd = 0u - static_cast<uint32_t>(gq & 1);
-    const uint32_t p = from_xor16(w[0], gq & 1);
-    const uint32_t ev = bitsel(m_odd, p, w[0]), od = bitsel(m_odd, w[0], p);   // the pair's even, odd lane words
-    const uint32_t lo = (ev & 0xffffu) | (od << 16);
-    uint32_t own = lo, send = lo;
-    if constexpr (BS == 32) {
-      const uint32_t hi = (ev >> 16) | (od & 0xffff0000u);
-      own = bitsel(0u - static_cast<uint32_t>(gq == 3), hi, lo);
-      send = bitsel(m_odd, lo, hi);
+    for (int q = 0; q < 4; ++q) {
+      xv[2 * q] = __uint_as_float(lo[q]);
+      xv[2 * q + 1] = __uint_as_float(hi[q]);
     }
-    const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
-    const uint32_t other = bitsel(0u - static_cast<uint32_t>(gq < 2), r[1], r[0]);
-    const uint32_t word = bitsel(0u - static_cast<uint32_t>(gq == 0 || gq == 3), own, other);
-    uint8_t* dst = codes + static_cast<size_t>(row) * (d_in / 2) + static_cast<size_t>(blk) * (BS / 2);
-    reinterpret_cast<uint32_t*>(dst)[BS == 32 ? gq : (gq & 1)] = word;
-    if constexpr (FMT == kMXP)
-      reinterpret_cast<uint8_t*>(scales)[mxfp4_plane_offset(row, blk, nblk / 8)] = static_cast<uint8_t>(q.scale);
-    else
-      store_scale<FMT>(scales, static_cast<size_t>(row) * nblk + blk, q.scale);
   }
 }
 
-template <int BS, int FMT, bool BF16>
-// (X and T are not declared __restrict__ here: the compiler moves
-// restrict-qualified loads freely and would issue x's before T's.)
-__global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_mfma_kernel(
-    const void* X, const float* T, int n, int d_in, float g,
-    uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t* __restrict__ amax_out,
-    const int* __restrict__ tmap, int ngroups) {
-  using U = XUnit<BS, BF16>;
-  constexpr int H = BS / 16, C = BS / 4, D = kMfmaDepth;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kWavesPerGroup * U::kLdsDwords];
+// A-operand fragments of one span: ta[h][c] = T[row][4c + g] for the rows
+// described above (bs 32), or of block h of the span (bs 16, c < 4).  Loaded
+// in raw form first (so that the loads of x can be issued before the wait for
+// T), then transposed like fp32 x.
+struct TRaw {
+  uint4 v[4];
+};
+
+template <int BS>
+__device__ __forceinline__ void load_t(const float* T, const int* tmap, int ngroups, int sp, int nblk, int q, int j,
+                                       TRaw& tr) {
+  if constexpr (BS == 32) {
+    const int b = min(sp, nblk - 1);
+    const int tsel = tmap ? min(max(tmap[b], 0), ngroups - 1) : b;
+    const float* Tb = T + static_cast<size_t>(tsel) * 1024;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4* p = reinterpret_cast<const uint4*>(Tb + (8 * (j >> 2) + 4 * h + (j & 3)) * 32 + 8 * q);
+      tr.v[2 * h] = p[0];
+      tr.v[2 * h + 1] = p[1];
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = min(2 * sp + h, nblk - 1);
+      const int tsel = tmap ? min(max(tmap[b], 0), ngroups - 1) : b;
+      tr.v[h] = *reinterpret_cast<const uint4*>(T + static_cast<size_t>(tsel) * 256 + j * 16 + 4 * q);
+    }
+  }
+}
+
+template <int BS>
+__device__ __forceinline__ void t_steps(const TRaw& tr, float (&ta)[2][8]) {
+  if constexpr (BS == 32) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 a = tr.v[2 * h], c = tr.v[2 * h + 1];
+      uint32_t lo[4] = {a.x, a.y, a.z, a.w}, hi[4] = {c.x, c.y, c.z, c.w};
+      transpose4(lo);
+      transpose4(hi);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ta[h][2 * k] = __uint_as_float(lo[k]);
+        ta[h][2 * k + 1] = __uint_as_float(hi[k]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t d[4] = {tr.v[h].x, tr.v[h].y, tr.v[h].z, tr.v[h].w};
+      transpose4(d);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ta[h][c] = __uint_as_float(d[c]);
+#pragma unroll
+      for (int c = 4; c < 8; ++c) ta[h][c] = 0.0f;
+    }
+  }
+}
+
+// The MFMA chains, block maxima, encoders and stores of one span of one unit.
+template <int BS, int FMT>
+__device__ __forceinline__ void span_unit(const float (&ta)[2][8], const float (&xv)[8], int sp, int nblk, int q,
+                                          const UnitRows& ur, int d_in, float g, uint8_t* __restrict__ codes,
+                                          void* __restrict__ scales, uint32_t& run_max) {
+  const int jj = ur.jj;
+  uint8_t* const cbase = codes + ur.row0 * (d_in / 2);                       // code rows of the unit
+  const int crow = jj * (d_in / 2);
+  v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  if constexpr (BS == 32) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[h][c], xv[c], acc[h], 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[h][c], xv[4 * h + c], acc[h], 0, 0, 0);
+  }
+  constexpr int QF = FMT == kMXP ? kMX : FMT;
+  if constexpr (BS == 32) {
+    const int b = min(sp, nblk - 1);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { y[e] = acc[0][e]; y[4 + e] = acc[1][e]; }
+    if constexpr (FMT == kApply) {
+      float* dst = reinterpret_cast<float*>(codes) + ur.row0 * d_in + static_cast<uint32_t>(jj * d_in + b * 32 + 8 * q);
+      reinterpret_cast<float4*>(dst)[0] = make_float4(y[0], y[1], y[2], y[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(y[4], y[5], y[6], y[7]);
+      return;
+    }
+    uint32_t ab = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
+    ab = max_groups(ab);
+    if constexpr (FMT == kAmax) {
+      run_max = max(run_max, ab);
+    } else {
+      const BlockQuant<QF> bq = block_quant<QF>(ab, g);
+      uint32_t w[1];
+      encode_pairs<QF, 4>(y, bq, w);
+      *reinterpret_cast<uint32_t*>(cbase + static_cast<uint32_t>(crow + b * 16 + 4 * q)) = w[0];
+      if constexpr (FMT == kMXP) {
+        // every row of the unit shares its 256-row tile and plane position: lane row jj adds 16 jj
+        uint8_t* sbase = reinterpret_cast<uint8_t*>(scales) + mxfp4_plane_offset(static_cast<int>(ur.row0), b, nblk / 8);
+        sbase[static_cast<uint32_t>(16 * jj)] = static_cast<uint8_t>(bq.scale);
+      } else {
+        store_scale<QF>(scales, ur.row0 * nblk + static_cast<uint32_t>(jj * nblk + b), bq.scale);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = min(2 * sp + h, nblk - 1);
+      float y[4] = {acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+      if constexpr (FMT == kApply) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(codes) + ur.row0 * d_in +
+                                   static_cast<uint32_t>(jj * d_in + b * 16 + 4 * q)) = make_float4(y[0], y[1], y[2], y[3]);
+        continue;
+      }
+      uint32_t ab = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
+      ab = max_groups(ab);
+      if constexpr (FMT == kAmax) {
+        run_max = max(run_max, ab);
+      } else {
+        const BlockQuant<QF> bq = block_quant<QF>(ab, g);
+        uint32_t w[1];
+        encode_pairs<QF, 2>(y, bq, w);
+        *reinterpret_cast<uint16_t*>(cbase + static_cast<uint32_t>(crow + b * 8 + 2 * q)) = static_cast<uint16_t>(w[0]);
+        store_scale<QF>(scales, ur.row0 * nblk + static_cast<uint32_t>(jj * nblk + b), bq.scale);
+      }
+    }
+  }
+}
+
+// Both spans of a unit at bs 32 (blocks b0 and b0 + 1, both inside d_in),
+// quantized, with their stores merged: the two code dwords of lane group g
+// (bytes 4g.. of block b0 and of block b0 + 1) are exchanged across the lane
+// groups so that group g holds bytes 8g .. 8g+7 of the token's 32-byte run,
+// one 8-byte store; the two scales go out in one store, lane groups 0 and 2
+// writing block b0's and groups 1 and 3 block b0 + 1's.
+template <int FMT>
+__device__ __forceinline__ void pair_unit(const float (&ta)[2][2][8], const float (&xv)[2][8], int b0, int nblk, int q,
+                                          const UnitRows& ur, int d_in, float g, uint8_t* __restrict__ codes,
+                                          void* __restrict__ scales) {
+  constexpr int QF = FMT == kMXP ? kMX : FMT;
+  uint32_t w[2], sc[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[s][h][c], xv[s][c], acc[h], 0, 0, 0);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { y[e] = acc[0][e]; y[4 + e] = acc[1][e]; }
+    uint32_t ab = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
+    ab = max_groups(ab);
+    const BlockQuant<QF> bq = block_quant<QF>(ab, g);
+    uint32_t ws[1];
+    encode_pairs<QF, 4>(y, bq, ws);
+    w[s] = ws[0];
+    sc[s] = bq.scale;
+  }
+  swap32(w[0], w[1]);
+  swap16(w[0], w[1]);
+  *reinterpret_cast<uint2*>(codes + ur.row0 * (d_in / 2) + static_cast<uint32_t>(ur.jj * (d_in / 2) + b0 * 16 + 8 * q)) =
+      make_uint2(w[0], w[1]);
+  const int odd = q & 1;
+  const uint32_t scale = odd ? sc[1] : sc[0];
+  if constexpr (FMT == kMXP) {
+    uint8_t* sbase = reinterpret_cast<uint8_t*>(scales) + mxfp4_plane_offset(static_cast<int>(ur.row0), b0 + odd, nblk / 8);
+    sbase[static_cast<uint32_t>(16 * ur.jj)] = static_cast<uint8_t>(scale);
+  } else {
+    store_scale<QF>(scales, ur.row0 * nblk + static_cast<uint32_t>(ur.jj * nblk + b0 + odd), scale);
+  }
+}
+
+// Does the merged-store pair path apply?  bs 32, a quantized format, and an
+// even number of blocks (so every wave's two blocks lie inside d_in and a
+// pair of 2-byte scales is aligned).
+constexpr bool pair_format(int bs, int fmt) { return bs == 32 && (fmt == kMX || fmt == kI4 || fmt == kMXP); }
+
+// One unit of all the wave's spans: merged stores (PAIR), else span by span.
+template <int BS, int FMT, bool PAIR>
+__device__ __forceinline__ void unit_out(const float (&ta)[kSpans][2][8], const float (&xv)[kSpans][8], int sp0,
+                                         int nblk, int q, const UnitRows& ur, int d_in, float g,
+                                         uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t& run_max) {
+  if constexpr (PAIR) {
+    static_assert(kSpans == 2 && pair_format(BS, FMT), "pair path: two bs-32 spans of a quantized format");
+    pair_unit<FMT>(ta, xv, sp0, nblk, q, ur, d_in, g, codes, scales);
+  } else {
+#pragma unroll
+    for (int s = 0; s < kSpans; ++s)
+      span_unit<BS, FMT>(ta[s], xv[s], sp0 + s, nblk, q, ur, d_in, g, codes, scales, run_max);
+  }
+}
+
+// (X and T are not declared __restrict__: restrict-qualified loads would be
+// moved freely across the scheduling fences.)
+template <int BS, int FMT, bool BF16, bool PAIR>
+__global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
+    const void* X, const float* T, int n, int d_in, float g, uint8_t* __restrict__ codes, void* __restrict__ scales,
+    uint32_t* __restrict__ amax_out, const int* __restrict__ tmap, int ngroups, int upw) {
+  constexpr int R = XRaw<BF16>::kDwords;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, q = lane >> 4;
   const int nblk = d_in / BS;
-  const int blk = blockIdx.x * kWavesPerGroup + wave;
-  if (blk >= nblk) return;                       // wave-uniform; the waves share no LDS and meet at no barrier
-  const int j = lane & 15, gq = lane >> 4;
-  uint32_t* const lt = lds + wave * U::kLdsDwords;   // T, row stride kTStride
-  uint32_t* const lx = lt + BS * U::kTStride;         // one unit of x
-  // T's pieces are requested first, then the first units of x, so that the
-  // wait for T (from L2) leaves the loads of x (from HBM) in flight
-  const size_t col = static_cast<size_t>(blk) * BS;
-  const int t0 = blockIdx.y * (kMfmaUnits * U::kRows);
-  uint32_t run_max = 0;
-  // the block's matrix, or with a group map its group's (ids clamped to the table)
-  const int tsel = tmap ? min(max(tmap[blk], 0), ngroups - 1) : blk;
-  const uint4* tp = reinterpret_cast<const uint4*>(T + static_cast<size_t>(tsel) * BS * BS);
-  constexpr int NT = BS * BS / 256;   // pieces of T per lane (4 or 1)
-  const uint4 tv0 = tp[lane];
-  const uint4 tv1 = NT > 1 ? tp[lane + 64] : tv0;
-  const uint4 tv2 = NT > 1 ? tp[lane + 128] : tv0;
-  const uint4 tv3 = NT > 1 ? tp[lane + 192] : tv0;
-  __builtin_amdgcn_sched_barrier(0);
-  uint32_t raw[D][U::kRaw];
+  const int nspans = (d_in + 31) / 32;
+  const int sp0 = (blockIdx.x * kWavesPerGroup + wave) * kSpans;
+  if (sp0 >= nspans) return;                      // wave-uniform; no barrier follows
+  const int u0 = blockIdx.y * upw;                // first unit (16 tokens) of this wave
+  int col[kSpans];
 #pragma unroll
-  for (int i = 0; i < D; ++i) load_unit<BS, BF16>(X, t0 + i * U::kRows, n, d_in, col, lane, raw[i]);
-  __builtin_amdgcn_sched_barrier(0);
-  // piece m = lane + 64 i of T: row m / (bs/4), columns 4 (m % (bs/4)) .. + 3
+  for (int s = 0; s < kSpans; ++s) col[s] = span_col<BS>(sp0 + s, q, nblk);
+  // T's loads first, then the first units of x; the wait for T (from L2)
+  // then leaves the loads of x (from HBM) in flight
+  TRaw traw[kSpans];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int m = lane + 64 * i;
-    *reinterpret_cast<uint4*>(lt + (m / (BS / 4)) * U::kTStride + 4 * (m % (BS / 4))) =
-        i == 0 ? tv0 : i == 1 ? tv1 : i == 2 ? tv2 : tv3;
+  for (int s = 0; s < kSpans; ++s) load_t<BS>(T, tmap, ngroups, sp0 + s, nblk, q, j, traw[s]);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t raw[kDepth][kSpans][R];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    const UnitRows ur = unit_rows(u0 + d, n, j);
+#pragma unroll
+    for (int s = 0; s < kSpans; ++s) load_x<BF16>(X, ur, d_in, col[s], raw[d][s]);
   }
-  float ta[H][C];
+  __builtin_amdgcn_sched_barrier(0);
+  float ta[kSpans][2][8];
 #pragma unroll
-  for (int h = 0; h < H; ++h)
+  for (int s = 0; s < kSpans; ++s) t_steps<BS>(traw[s], ta[s]);
+  uint32_t run_max = 0;
+  // Units u0 .. u0 + upw - 1 (upw a multiple of kDepth), the last kDepth of
+  // them without refills.
+  int u = 0;
+#pragma unroll 1
+  for (; u + kDepth < upw; u += kDepth) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) ta[h][c] = __uint_as_float(lt[(16 * h + j) * U::kTStride + 4 * c + gq]);
-  // Fully unrolled, so that every wait counts exactly the loads and stores
-  // issued after the one it waits for.  Units past n repeat row n - 1, whose
-  // bytes they write again unchanged.
+    for (int d = 0; d < kDepth; ++d) {
+      float xv[kSpans][8];
 #pragma unroll
-  for (int u = 0; u < kMfmaUnits; ++u) {
-    const int tb = t0 + u * U::kRows;
-    if constexpr (BF16) stage_unit<BS>(lx, lane, raw[u % D]);
-    float xv[U::kGroups][C];
+      for (int s = 0; s < kSpans; ++s) x_steps<BF16>(raw[d][s], xv[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      const UnitRows un = unit_rows(u0 + u + d + kDepth, n, j);
 #pragma unroll
-    for (int s = 0; s < U::kGroups; ++s) group_x<BS, BF16>(lx, raw[u % D], s, lane, xv[s]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (u + D < kMfmaUnits) load_unit<BS, BF16>(X, tb + D * U::kRows, n, d_in, col, lane, raw[u % D]);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < kSpans; ++s) load_x<BF16>(X, un, d_in, col[s], raw[d][s]);
+      __builtin_amdgcn_sched_barrier(0);
+      const UnitRows ur = unit_rows(u0 + u + d, n, j);
+      unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, ur, d_in, g, codes, scales, run_max);
+    }
+  }
 #pragma unroll
-    for (int s = 0; s < U::kGroups; ++s)
-      mfma_group<BS, FMT>(ta, xv[s], gq, min(tb + 16 * s + j, n - 1), blk, nblk, d_in, g, codes, scales, run_max);
+  for (int d = 0; d < kDepth; ++d) {
+    float xv[kSpans][8];
+#pragma unroll
+    for (int s = 0; s < kSpans; ++s) x_steps<BF16>(raw[d][s], xv[s]);
+    const UnitRows ur = unit_rows(u0 + u + d, n, j);
+    unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, ur, d_in, g, codes, scales, run_max);
   }
   if constexpr (FMT == kAmax) {
 #pragma unroll
@@ -661,38 +767,69 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_hd_kernel(
 __global__ void fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
 using KernelFn = void (*)(const void*, const float*, int, int, float, uint8_t*, void*, uint32_t*, const int*, int);
+using DenseFn = void (*)(const void*, const float*, int, int, float, uint8_t*, void*, uint32_t*, const int*, int, int);
+using IdentFn = void (*)(const void*, int, int, float, uint8_t*, void*, uint32_t*);
 
-// bf16 x: the matrix-core kernel.  fp32 x still reads every fourth element
-// with scattered dword loads there (no LDS transpose yet), which is slower
-// than the vector-ALU kernel, so fp32 x keeps the latter.
 template <int BS, int FMT>
-KernelFn pick(bool bf16, bool ident) {
-  if (bf16) return ident ? tq_kernel<BS, FMT, true, true> : tq_mfma_kernel<BS, FMT, true>;
-  return ident ? tq_kernel<BS, FMT, false, true> : tq_kernel<BS, FMT, false, false>;
+DenseFn dense(bool bf16, bool pair) {
+  if constexpr (pair_format(BS, FMT)) {
+    if (pair) return bf16 ? tq_dense_kernel<BS, FMT, true, true> : tq_dense_kernel<BS, FMT, false, true>;
+  }
+  return bf16 ? tq_dense_kernel<BS, FMT, true, false> : tq_dense_kernel<BS, FMT, false, false>;
 }
 
-KernelFn select_kernel(int fmt, int bs, bool bf16, bool ident) {
-  if (fmt == kMXP) return (bs == 32 && !ident) ? (bf16 ? tq_mfma_kernel<32, kMXP, true> : tq_mfma_kernel<32, kMXP, false>)
-                                              : nullptr;
-  if (fmt == kApply) {
-    if (ident) return nullptr;
-    if (bs == 32) return bf16 ? tq_mfma_kernel<32, kApply, true> : tq_mfma_kernel<32, kApply, false>;
-    if (bs == 16) return bf16 ? tq_mfma_kernel<16, kApply, true> : tq_mfma_kernel<16, kApply, false>;
-    return nullptr;
-  }
+DenseFn select_dense(int fmt, int bs, bool bf16, int nblk) {
+  const bool pair = nblk % 2 == 0;
   if (bs == 32) {
     switch (fmt) {
-      case kMX: return pick<32, kMX>(bf16, ident);
-      case kI4: return pick<32, kI4>(bf16, ident);
-      case kAmax: return pick<32, kAmax>(bf16, ident);
+      case kMX: return dense<32, kMX>(bf16, pair);
+      case kI4: return dense<32, kI4>(bf16, pair);
+      case kAmax: return dense<32, kAmax>(bf16, pair);
+      case kApply: return dense<32, kApply>(bf16, pair);
+      case kMXP: return dense<32, kMXP>(bf16, pair);
     }
   } else if (bs == 16) {
     switch (fmt) {
-      case kNV: return pick<16, kNV>(bf16, ident);
-      case kAmax: return pick<16, kAmax>(bf16, ident);
+      case kNV: return dense<16, kNV>(bf16, pair);
+      case kAmax: return dense<16, kAmax>(bf16, pair);
+      case kApply: return dense<16, kApply>(bf16, pair);
     }
   }
   return nullptr;
+}
+
+template <int BS, int FMT>
+IdentFn ident(bool bf16) { return bf16 ? tq_ident_kernel<BS, FMT, true> : tq_ident_kernel<BS, FMT, false>; }
+
+IdentFn select_ident(int fmt, int bs, bool bf16) {
+  if (bs == 32) {
+    switch (fmt) {
+      case kMX: return ident<32, kMX>(bf16);
+      case kI4: return ident<32, kI4>(bf16);
+      case kAmax: return ident<32, kAmax>(bf16);
+    }
+  } else if (bs == 16) {
+    switch (fmt) {
+      case kNV: return ident<16, kNV>(bf16);
+      case kAmax: return ident<16, kAmax>(bf16);
+    }
+  }
+  return nullptr;
+}
+
+// Units (16 tokens) per wave of the dense kernel: about eight waves per SIMD
+// over the whole grid, at least kDepth units each, a multiple of kDepth.
+int dense_units_per_wave(int n, int d_in) {
+  const long units = (n + 15) / 16;
+  const long span_groups = ((d_in + 31) / 32 + kSpans - 1) / kSpans;
+  const long wave_cols = (span_groups + kWavesPerGroup - 1) / kWavesPerGroup * kWavesPerGroup;
+  const long target_waves = 8L * 4 * 256;     // 8 waves on each of the 1024 SIMDs
+  const long slices = std::max(1L, target_waves / wave_cols);
+  long upw = (units + slices - 1) / slices;
+  upw = (upw + kDepth - 1) / kDepth * kDepth;
+  upw = std::max<long>(upw, kDepth);
+  while ((units + upw - 1) / upw > 65535) upw += kDepth;
+  return static_cast<int>(upw);
 }
 
 wush_status launch(int fmt, int bs, bool bf16, int n, int d_in, const void* X, const float* T, float g,
@@ -700,17 +837,22 @@ wush_status launch(int fmt, int bs, bool bf16, int n, int d_in, const void* X, c
                    int ngroups = 0) {
   if (n == 0) return WUSH_OK;
   if (!wush::aligned16(T)) return wush::fail(WUSH_E_ARG, "transform_quant: T must be 16-byte aligned");
-  KernelFn k = select_kernel(fmt, bs, bf16, T == nullptr);
-  if (!k) return wush::fail(WUSH_E_UNSUPPORTED, "transform_quant: no kernel for fmt=%d bs=%d", fmt, bs);
-  const int nblk = d_in / bs;
-  const bool mfma = T && (bf16 || fmt == kApply || fmt == kMXP);
-  const int per_wave = !mfma ? kTokensPerWave
-                       : kMfmaUnits * (bs == 32 ? (bf16 ? XUnit<32, true>::kRows : XUnit<32, false>::kRows)
-                                                : (bf16 ? XUnit<16, true>::kRows : XUnit<16, false>::kRows));
-  dim3 grid((nblk + kWavesPerGroup - 1) / kWavesPerGroup, (n + per_wave - 1) / per_wave);
-  if (grid.y > 65535u) return wush::fail(WUSH_E_SHAPE, "transform_quant: n=%d too large", n);
-  hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, T, n, d_in, g, codes, scales, amax, tmap,
-                     ngroups);
+  if (!T) {
+    IdentFn k = select_ident(fmt, bs, bf16);
+    if (!k) return wush::fail(WUSH_E_UNSUPPORTED, "transform_quant: no identity kernel for fmt=%d bs=%d", fmt, bs);
+    const int nblk = d_in / bs;
+    dim3 grid((nblk + kWavesPerGroup - 1) / kWavesPerGroup, (n + kTokensPerWave - 1) / kTokensPerWave);
+    if (grid.y > 65535u) return wush::fail(WUSH_E_SHAPE, "transform_quant: n=%d too large", n);
+    hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, n, d_in, g, codes, scales, amax);
+  } else {
+    DenseFn k = select_dense(fmt, bs, bf16, d_in / bs);
+    if (!k) return wush::fail(WUSH_E_UNSUPPORTED, "transform_quant: no kernel for fmt=%d bs=%d", fmt, bs);
+    const int upw = dense_units_per_wave(n, d_in);
+    const int span_groups = ((d_in + 31) / 32 + kSpans - 1) / kSpans;
+    dim3 grid((span_groups + kWavesPerGroup - 1) / kWavesPerGroup, ((n + 15) / 16 + upw - 1) / upw);
+    hipLaunchKernelGGL(k, grid, dim3(kWave * kWavesPerGroup), 0, stream, X, T, n, d_in, g, codes, scales, amax, tmap,
+                       ngroups, upw);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return wush::fail(WUSH_E_HIP, "transform_quant launch: %s", hipGetErrorString(e));
   return WUSH_OK;
