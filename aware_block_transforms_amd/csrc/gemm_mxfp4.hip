@@ -25,6 +25,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "common.h"
@@ -269,10 +270,11 @@ struct GemmCtx {
 };
 
 __device__ __forceinline__ void load_op(__amdgpu_buffer_rsrc_t rd, uint32_t d_off, __amdgpu_buffer_rsrc_t rs,
-                                        uint32_t s_off, uint32_t step8, int k, Stage& g) {
+                                        uint32_t s_off, uint32_t step8, int k, Stage& g, uint32_t dbase = 0,
+                                        uint32_t sbase = 0) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) g.d[u] = load16(rd, d_off, static_cast<uint32_t>(k) * 128 + u * step8);
-  g.s = load8(rs, s_off, static_cast<uint32_t>(k) * kScaleOp);
+  for (int u = 0; u < 8; ++u) g.d[u] = load16(rd, d_off, dbase + static_cast<uint32_t>(k) * 128 + u * step8);
+  g.s = load8(rs, s_off, sbase + static_cast<uint32_t>(k) * kScaleOp);
 }
 
 // one operand (op 0 = A, 1 = B) of a block into the LDS buffer `buf`
@@ -331,20 +333,21 @@ __device__ __forceinline__ void mfma_column(const Frags& f, v4f (&acc)[8][8]) {
 template <int Q>
 __device__ __forceinline__ void slot(const GemmCtx& c, const uint8_t* rbuf, int rj, uint8_t* fb, uint2* sp,
                                      __amdgpu_buffer_rsrc_t rd, uint32_t d_off, __amdgpu_buffer_rsrc_t rs,
-                                     uint32_t s_off, uint32_t lk, const Frags& cur, Frags& nxt, Stage& st,
-                                     v4f (&acc)[8][8]) {
+                                     uint32_t s_off, uint32_t dso, uint32_t sso, const Frags& cur, Frags& nxt,
+                                     Stage& st, v4f (&acc)[8][8]) {
   mfma_iq<0, Q>(cur, acc[0][Q]);
-  if (Q < 4) nxt.b[2 * Q] = *reinterpret_cast<const uint4*>(rbuf + kFragOp + (c.wn * 8 + 2 * Q) * 2048 + c.r_frag[rj]);
+  if constexpr (Q < 4)
+    nxt.b[2 * Q] = *reinterpret_cast<const uint4*>(rbuf + kFragOp + (c.wn * 8 + 2 * Q) * 2048 + c.r_frag[rj]);
   mfma_iq<1, Q>(cur, acc[1][Q]);
-  if (Q < 4)
+  if constexpr (Q < 4)
     nxt.b[2 * Q + 1] = *reinterpret_cast<const uint4*>(rbuf + kFragOp + (c.wn * 8 + 2 * Q + 1) * 2048 + c.r_frag[rj]);
   *reinterpret_cast<uint4*>(fb + (Q >> 1) * 2048 + ((Q & 1) ? c.w_frag1 : c.w_frag0)) = st.d[Q];
   mfma_iq<2, Q>(cur, acc[2][Q]);
-  st.d[Q] = load16(rd, d_off, lk * 128 + Q * c.row_step8);
+  st.d[Q] = load16(rd, d_off, dso + Q * c.row_step8);
   mfma_iq<3, Q>(cur, acc[3][Q]);
   if (Q == 6) *sp = st.s;
   mfma_iq<4, Q>(cur, acc[4][Q]);
-  if (Q == 7) st.s = load8(rs, s_off, lk * kScaleOp);
+  if (Q == 7) st.s = load8(rs, s_off, sso);
   mfma_iq<5, Q>(cur, acc[5][Q]);
   mfma_iq<6, Q>(cur, acc[6][Q]);
   mfma_iq<7, Q>(cur, acc[7][Q]);
@@ -354,10 +357,12 @@ __device__ __forceinline__ void slot(const GemmCtx& c, const uint8_t* rbuf, int 
 
 // One phase: the MFMAs of the current sub-step on `cur`; meanwhile sub-step
 // (rbuf, rj) into `nxt`, operand `op` of the block staged in `st` written to
-// `wbuf`, and `st` reloaded with block `lk` of that operand.
+// `wbuf`, and `st` reloaded from the block at byte offsets dso (codes) and
+// sso (scale planes) past the lane's own offsets.
 template <bool kBarrier>
-__device__ __forceinline__ void phase(const GemmCtx& c, const uint8_t* rbuf, int rj, uint8_t* wbuf, int op, int lk,
-                                      Frags& cur, Frags& nxt, Stage& st, v4f (&acc)[8][8]) {
+__device__ __forceinline__ void phase(const GemmCtx& c, const uint8_t* rbuf, int rj, uint8_t* wbuf, int op,
+                                      uint32_t dso, uint32_t sso, Frags& cur, Frags& nxt, Stage& st,
+                                      v4f (&acc)[8][8]) {
   __builtin_amdgcn_sched_barrier(0);
   nxt.sa = *reinterpret_cast<const uint2*>(rbuf + 2 * kFragOp + rj * 1024 + c.r_scale_a);
   nxt.sb = *reinterpret_cast<const uint2*>(rbuf + 2 * kFragOp + kScaleOp + rj * 1024 + c.r_scale_b);
@@ -365,15 +370,14 @@ __device__ __forceinline__ void phase(const GemmCtx& c, const uint8_t* rbuf, int
   uint2* const sp = reinterpret_cast<uint2*>(wbuf + 2 * kFragOp + op * kScaleOp + c.w_scale);
   const __amdgpu_buffer_rsrc_t rd = op ? c.rb : c.ra, rs = op ? c.rsb : c.rsa;
   const uint32_t d_off = op ? c.b_off : c.a_off, s_off = op ? c.sb_off : c.sa_off;
-  const uint32_t k = static_cast<uint32_t>(lk);
-  slot<0>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
-  slot<1>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
-  slot<2>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
-  slot<3>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
-  slot<4>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
-  slot<5>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
-  slot<6>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
-  slot<7>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, k, cur, nxt, st, acc);
+  slot<0>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, dso, sso, cur, nxt, st, acc);
+  slot<1>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, dso, sso, cur, nxt, st, acc);
+  slot<2>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, dso, sso, cur, nxt, st, acc);
+  slot<3>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, dso, sso, cur, nxt, st, acc);
+  slot<4>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, dso, sso, cur, nxt, st, acc);
+  slot<5>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, dso, sso, cur, nxt, st, acc);
+  slot<6>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, dso, sso, cur, nxt, st, acc);
+  slot<7>(c, rbuf, rj, fb, sp, rd, d_off, rs, s_off, dso, sso, cur, nxt, st, acc);
   if (kBarrier) phase_barrier();
 }
 
@@ -500,11 +504,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restri
     uint8_t* const cb = (k & 1) ? buf1 : buf0;   // block k
     uint8_t* const nb = (k & 1) ? buf0 : buf1;   // block k + 1
     // sub-step (k, 0); read (k, 1); write B(k+1); load B(k+2); barrier
-    phase<true>(c, cb, 1, nb, 1, min(k + 2, last), f0, f1, sb, acc);
+    const uint32_t kb = static_cast<uint32_t>(min(k + 2, last)), ka = static_cast<uint32_t>(min(k + 3, last));
+    phase<true>(c, cb, 1, nb, 1, kb * 128, kb * kScaleOp, f0, f1, sb, acc);
     // sub-step (k, 1); read (k+1, 0); write A(k+2) into block k's buffer; load A(k+3).
     // No barrier: block k's buffer was last read before the barrier above,
     // and A(k+2) is next read after the barrier that ends the next phase.
-    phase<false>(c, nb, 0, cb, 0, min(k + 3, last), f1, f0, sa, acc);
+    phase<false>(c, nb, 0, cb, 0, ka * 128, ka * kScaleOp, f1, f0, sa, acc);
     ++k;
   } while (k < nfull);
   if (half) {   // sub-step (nfull, 0), read by the last phase
@@ -533,6 +538,158 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_lds(const uint8_t* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form of the LDS kernel (K a multiple of 256, at least 4 blocks):
+// one workgroup per CU walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+// (the same XCD-aware order, and the same XCD, since a workgroup id keeps its
+// residue mod 8), and the software pipeline runs on across tile boundaries:
+// the loads that would fall past a tile's last K block fetch the next tile's
+// first blocks instead, so the next tile's first LDS block and fragments are
+// ready when its MFMAs start.  Between tiles the wave only stores its output
+// tile and clears its accumulators.  Buffer parity follows the global block
+// count.  Offsets: a loader lane's own part (row within the tile, chunk) is in
+// its voffset, the tile and block part in the scalar soffset.
+struct TileBase {
+  uint32_t a, b;      // code bytes of the tile's first A / B row
+  uint32_t sa, sb;    // plane-ordered scale bytes of the tile's row tiles, block 0
+  int m0, n0;
+};
+
+__device__ __forceinline__ TileBase tile_base(int id, int tiles_m, int tiles_n, int nb, uint32_t krow) {
+  int tm, tn;
+  tile_of(id, tiles_m, tiles_n, tm, tn);
+  TileBase t;
+  t.m0 = tm * kBM;
+  t.n0 = tn * kBN;
+  t.a = static_cast<uint32_t>(t.m0) * krow;
+  t.b = static_cast<uint32_t>(t.n0) * krow;
+  t.sa = static_cast<uint32_t>(tm * nb) * kScaleOp;
+  t.sb = static_cast<uint32_t>(tn * nb) * kScaleOp;
+  return t;
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_mxfp4_persist(const uint8_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ PA,
+                                                            const uint8_t* __restrict__ B,
+                                                            const uint8_t* __restrict__ PB, float* __restrict__ Y,
+                                                            int M, int N, int K) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
+  GemmCtx c;
+  const int lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.wm = c.wave >> 1;
+  c.wn = c.wave & 1;
+  c.nb = K / 256;                             // >= 4 (checked by the launcher)
+  const int nb = c.nb;
+  const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+  const int ntiles = tiles_m * tiles_n;
+  const int step = gridDim.x;
+  int t = blockIdx.x;
+  if (t >= ntiles) return;                    // workgroup-uniform
+  const int rr = lane & 15, grp = lane >> 4;
+  const uint32_t krow = static_cast<uint32_t>(K) / 2;
+  const int lr = lane >> 3, lc = lane & 7;
+  c.a_off = static_cast<uint32_t>(64 * c.wave + lr) * krow + lc * 16;
+  c.b_off = c.a_off;
+  c.row_step8 = 8 * krow;
+  c.w_frag0 = lr * 128 + ((lc ^ ((lr >> 1) & 7)) * 16);
+  c.w_frag1 = (lr + 8) * 128 + ((lc ^ (((lr + 8) >> 1) & 7)) * 16);
+  c.w_scale = c.wave * 512 + lane * 8;
+  c.sa_off = c.w_scale;
+  c.sb_off = c.w_scale;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) c.r_frag[j] = rr * 128 + ((((4 * j + grp) ^ ((rr >> 1) & 7))) * 16);
+  c.r_scale_a = grp * 256 + rr * 16 + ((c.wm * 8) ^ (8 * (grp & 1)));
+  c.r_scale_b = grp * 256 + rr * 16 + ((c.wn * 8) ^ (8 * (grp & 1)));
+  c.ra = make_rsrc(A, static_cast<uint32_t>(M) * krow);
+  c.rb = make_rsrc(B, static_cast<uint32_t>(N) * krow);
+  c.rsa = make_rsrc(PA, static_cast<uint32_t>(tiles_m * nb) * kScaleOp);
+  c.rsb = make_rsrc(PB, static_cast<uint32_t>(tiles_n * nb) * kScaleOp);
+
+  TileBase cur = tile_base(t, tiles_m, tiles_n, nb, krow);
+  TileBase nxt = tile_base(t + step < ntiles ? t + step : t, tiles_m, tiles_n, nb, krow);
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[i][q] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* const buf0 = smem;
+  uint8_t* const buf1 = smem + kStageBytes;
+  // prologue of the first tile, as in the per-tile kernel
+  Stage sa, sb;
+  Frags f0, f1;
+  load_op(c.ra, c.a_off, c.rsa, c.sa_off, c.row_step8, 0, sa, cur.a, cur.sa);
+  load_op(c.rb, c.b_off, c.rsb, c.sb_off, c.row_step8, 0, sb, cur.b, cur.sb);
+  __builtin_amdgcn_sched_barrier(0);
+  write_op(c, buf0, 0, sa);
+  write_op(c, buf0, 1, sb);
+  __builtin_amdgcn_sched_barrier(0);
+  load_op(c.ra, c.a_off, c.rsa, c.sa_off, c.row_step8, 1, sa, cur.a, cur.sa);
+  __builtin_amdgcn_sched_barrier(0);
+  load_op(c.rb, c.b_off, c.rsb, c.sb_off, c.row_step8, 1, sb, cur.b, cur.sb);
+  __builtin_amdgcn_sched_barrier(0);
+  write_op(c, buf1, 0, sa);
+  __builtin_amdgcn_sched_barrier(0);
+  load_op(c.ra, c.a_off, c.rsa, c.sa_off, c.row_step8, 2, sa, cur.a, cur.sa);
+  phase_barrier();
+  read_b_scales(c, buf0, 0, f0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) f0.a[q] = read_a(c, buf0, 0, q);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  int par = 0;                                // LDS buffer of the current block
+#pragma unroll 1
+  for (;;) {
+    int k = 0;
+#pragma unroll 1
+    do {
+      uint8_t* const cb = par ? buf1 : buf0;
+      uint8_t* const nb_ = par ? buf0 : buf1;
+      // blocks k + 2 (B) and k + 3 (A) of this tile, or of the next one past the end
+      const int jb = k + 2, ja = k + 3;
+      const uint32_t dso_b = jb < nb ? cur.b + jb * 128u : nxt.b + (jb - nb) * 128u;
+      const uint32_t sso_b = jb < nb ? cur.sb + jb * kScaleOp : nxt.sb + (jb - nb) * kScaleOp;
+      const uint32_t dso_a = ja < nb ? cur.a + ja * 128u : nxt.a + (ja - nb) * 128u;
+      const uint32_t sso_a = ja < nb ? cur.sa + ja * kScaleOp : nxt.sa + (ja - nb) * kScaleOp;
+      phase<true>(c, cb, 1, nb_, 1, dso_b, sso_b, f0, f1, sb, acc);
+      phase<false>(c, nb_, 0, cb, 0, dso_a, sso_a, f1, f0, sa, acc);
+      par ^= 1;
+      ++k;
+    } while (k < nb);
+
+    // lane holds Y[m0 + 128 wm + 16 q + rr][n0 + 128 wn + 16 i + 4 grp + 0..3]
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int m = cur.m0 + c.wm * 128 + q * 16 + rr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = cur.n0 + c.wn * 128 + i * 16 + 4 * grp;
+        float* dst = Y + static_cast<size_t>(m) * N + n;
+        if (n + 3 < N && (N & 3) == 0) {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[i][q][0], acc[i][q][1], acc[i][q][2], acc[i][q][3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) dst[e] = acc[i][q][e];
+        }
+      }
+    }
+    t += step;
+    if (t >= ntiles) break;
+    cur = nxt;
+    nxt = tile_base(t + step < ntiles ? t + step : t, tiles_m, tiles_n, nb, krow);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[i][q] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // surplus staging loads
+}
+
 }  // namespace
 
 namespace wush {
@@ -542,6 +699,35 @@ namespace {
 // K half-steps
 bool use_lds_kernel(int M, int N, int K) {
   return static_cast<long>(M) * (K / 2) < (1L << 31) && static_cast<long>(N) * (K / 2) < (1L << 31) && K >= 256;
+}
+
+// Persistent form: whole 256-wide K blocks, at least four of them
+bool use_persistent(int K) { return K % 256 == 0 && K / 256 >= 4; }
+
+// Compute units of the current device (one persistent workgroup each),
+// queried once per device.  (Concurrent first calls store the same value.)
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
+
+// The LDS kernel on plane-ordered scales PA / PB: persistent when it applies
+void launch_lds(int M, int N, int K, const uint8_t* A, const uint8_t* PA, const uint8_t* B, const uint8_t* PB,
+                float* Y, long tiles, hipStream_t stream) {
+  if (use_persistent(K)) {
+    const long grid = std::min<long>(tiles, device_cus());
+    hipLaunchKernelGGL(gemm_mxfp4_persist, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, A, PA, B, PB, Y,
+                       M, N, K);
+  } else {
+    hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, PA, B, PB, Y, M,
+                       N, K);
+  }
 }
 }  // namespace
 
@@ -570,8 +756,7 @@ wush_status gemm_mxfp4_planes(int M, int N, int K, const uint8_t* A, const uint8
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   const long tiles = static_cast<long>(tiles_m) * tiles_n;
   if (tiles > 0x7fffffffL) return fail(WUSH_E_SHAPE, "wush_w4a4_gemm_mx_planes: too many tiles");
-  hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, PA, B, PB, Y, M, N,
-                     K);
+  launch_lds(M, N, K, A, PA, B, PB, Y, tiles, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm_mx_planes launch: %s", hipGetErrorString(e));
   return WUSH_OK;
@@ -597,8 +782,7 @@ wush_status gemm_mxfp4(int M, int N, int K, const uint8_t* A, const uint8_t* SA,
     }
     hipLaunchKernelGGL(scales_to_planes, dim3(tiles_m + tiles_n, (nb + 1) / 2), dim3(256), 0, stream, SA, M, SB, N,
                        tiles_m, K, nb, P);
-    hipLaunchKernelGGL(gemm_mxfp4_lds, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, A, P, B,
-                       P + pa_bytes, Y, M, N, K);
+    launch_lds(M, N, K, A, P, B, P + pa_bytes, Y, tiles, stream);
     const hipError_t e = hipGetLastError();
     const hipError_t f = ws ? hipSuccess : hipFreeAsync(P, stream);
     if (e != hipSuccess) return fail(WUSH_E_HIP, "wush_w4a4_gemm launch: %s", hipGetErrorString(e));

@@ -16,7 +16,7 @@ import torch
 
 import aware_block_transforms_amd as W
 from oracle import quant, transforms as tr, gemm as og, had256 as oh
-from synth.gen import CONFIGS, make_weights, make_activations, bf16_bits
+from synth.gen import CONFIGS, make_weights, make_activations, bf16_bits, bf16_round
 from gpu_util import DEV, to_dev, x_dev, host, scales_np, gemm_close
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
@@ -186,3 +186,34 @@ def test_fullsize_had256():
     W.wush_had256_rotate(a, a)
     torch.cuda.synchronize()
     assert np.array_equal(host(a), ints)
+
+
+def test_fullsize_had256_outlier_activations():
+    # Activations with outlier channels (x50 on 0.1% of the 4096 channels, plus
+    # one channel at x1000): the GEMV rotates and splits the activations per
+    # 256-chunk into two int8 terms, whose rounding error grows with the chunk
+    # maximum, so the criterion is checked where the maximum is largest.
+    wl = CONFIGS["had256"]
+    Wt = make_weights(wl)
+    d_out, d_in = Wt.shape
+    print(f"[fullsize] {wl.name} outlier activations d_in={d_in} d_out={d_out}", flush=True)
+    nv, nrb = d_in // 256, d_out // 16
+    packed = torch.empty((W.wush_had256_packed_bytes(d_out, d_in),), dtype=torch.uint8, device=DEV)
+    W.wush_had256_pack_weights(to_dev(Wt), packed)
+    torch.cuda.synchronize()
+    blocks = _sample(nrb, 6, 7)
+    rows = (16 * blocks[:, None] + np.arange(16)).ravel()
+    rp = oh.pack_weights(Wt[rows])
+    rng = np.random.default_rng([5, 9])
+    ch = rng.choice(d_in, 5, replace=False)
+    for B in wl.extra["batches"]:
+        x = make_activations(wl, n=B)
+        x[:, ch[:4]] *= 50.0
+        x[:, ch[4]] *= 1000.0
+        x = bf16_round(x)
+        y = torch.full((B, d_out), np.nan, dtype=torch.float32, device=DEV)
+        W.wush_had256_gemv(to_dev(bf16_bits(x).view(np.int16)), packed, y)
+        torch.cuda.synchronize()
+        ref = oh.gemv(x, rp, len(rows))
+        ok, worst = gemm_close(host(y)[:, rows], ref)
+        assert ok, (B, worst)

@@ -176,6 +176,34 @@ def test_build_transforms_on_device_equals_host_builder(bs):
     assert e.value.status == W.WUSH_E_NUMERIC
 
 
+@pytest.mark.parametrize("bs", [32, 16])
+def test_build_transforms_on_device_matches_oracle(bs):
+    # the device builder against the oracle's own construction (LAPACK Cholesky
+    # and eigh in fp64): a few fp32 ulps of each block's largest entry and the
+    # same proxy loss
+    Wt, X = random_case(720 + bs, 400, 8 * bs, 112)
+    Wt[:, bs:2 * bs] *= np.float32(1e-3)                    # a badly scaled block
+    Sx = tr.activation_moments(X, bs).astype(np.float32)
+    nblk = Wt.shape[1] // bs
+    A = tr.weight_moments(Wt, bs)
+    for kind in ("identity", "hadamard", "wus", "wush"):
+        dx = torch.empty((nblk, bs, bs), dtype=torch.float32, device=DEV)
+        dw = torch.empty_like(dx)
+        W.wush_build_transforms_dev(kind, bs, to_dev(Wt), to_dev(Sx), dx, dw)
+        ex, ew = host(dx), host(dw)
+        rx, rw, _, _ = tr.build_transforms(kind, Wt, Sx, bs)
+        if kind in ("identity", "hadamard"):
+            assert np.array_equal(ex, rx) and np.array_equal(ew, rw), kind
+            continue
+        for T, R in ((ex, rx), (ew, rw)):
+            tol = 8 * 2.0 ** -24 * np.abs(R).max(axis=(1, 2), keepdims=True)
+            assert np.all(np.abs(T - R) <= tol), (kind, np.abs(T - R).max())
+        for b in range(nblk):
+            j_d = tr.proxy_loss(ew[b].astype(np.float64), A[b], Sx[b].astype(np.float64))
+            j_o = tr.proxy_loss(rw[b].astype(np.float64), A[b], Sx[b].astype(np.float64))
+            assert np.isclose(j_d, j_o, rtol=1e-5), (kind, b)
+
+
 def _planes_np(S):
     """Row-major E8M0 scales [rows][K/32] -> the matmul's plane order (layout of wush.h)."""
     rows, G = S.shape
@@ -424,6 +452,24 @@ def test_w4a4_gemm(fmt, shape):
         assert ok, (fmt, shape, w is None, worst)
 
 
+@pytest.mark.parametrize("shape", [(4600, 4090, 1024), (250, 66001, 1024)])
+def test_w4a4_gemm_more_tiles_than_workgroups(shape):
+    # more 256 x 256 output tiles than compute units: the MXFP4 kernel's
+    # workgroups each walk several tiles, with the loads of a tile's last
+    # blocks fetching the next tile's first ones; ragged M and N (N % 4 != 0)
+    M, N, K = shape
+    ca, sa, cb, sb, _, _ = _rand_operands("mxfp4", M, N, K, 3)
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    ref = og.w4a4_gemm_rows("mxfp4", rows, ca, sa, cb, sb)
+    Y = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+    W.wush_w4a4_gemm("mxfp4", to_dev(ca), to_dev(sa), to_dev(cb), to_dev(sb), Y)
+    torch.cuda.synchronize()
+    Yh = host(Y)
+    assert not np.isnan(Yh).any()
+    ok, worst = gemm_close(Yh[rows], ref)
+    assert ok, (shape, worst)
+
+
 def test_w4a4_gemm_workspace_checks():
     M, N, K = 300, 260, 512
     ca, sa, cb, sb, _, _ = _rand_operands("mxfp4", M, N, K, 2)
@@ -507,3 +553,29 @@ def test_had256_gemv(batch, d_in):
         torch.cuda.synchronize()
         ok, worst = gemm_close(host(y), ref)
         assert ok, (w is None, worst)
+
+
+@pytest.mark.parametrize("fmt,kind", [("mxfp4", "wush"), ("nvfp4", "wus"), ("int4", "hadamard"), ("mxfp4", "identity")])
+def test_w4a4_layer_helper_matches_oracle(fmt, kind):
+    # aware_block_transforms_amd.layer.W4A4Layer: host-built transforms, packed
+    # weights, then quantize + matmul through the library calls
+    from aware_block_transforms_amd.layer import W4A4Layer
+    bs = W.BLOCK[fmt]
+    Wt, X = random_case(810, 150, 256, 200)
+    Sx = tr.activation_moments(X, bs).astype(np.float32)
+    Tx, Tw, _, _ = tr.build_transforms(kind, Wt, Sx, bs)     # the oracle's pair, fed to both sides
+    L = W4A4Layer(fmt, kind, Wt, Tx=Tx, Tw=Tw)
+    Xd = to_dev(X)
+    ident = kind == "identity"
+    gx = None
+    if fmt == "nvfp4":
+        assert np.float32(L.calibrate(Xd)) == quant.nvfp4_tensor_scale(quant.apply_transform(Tx, X, identity=ident))
+        gx = np.float32(L.x_g)
+    gw = quant.nvfp4_tensor_scale(quant.apply_transform(Tw, Wt, identity=ident)) if fmt == "nvfp4" else None
+    wc, ws_ = quant.transform_quant(fmt, Tw, Wt, g=gw, identity=ident)
+    assert np.array_equal(host(L.w_codes), wc) and np.array_equal(scales_np(L.w_scales, fmt), ws_)
+    Y = L.forward(Xd)
+    torch.cuda.synchronize()
+    xc, xs = quant.transform_quant(fmt, Tx, X, g=gx, identity=ident)
+    ok, worst = gemm_close(host(Y), og.w4a4_gemm(fmt, xc, xs, wc, ws_, gx, gw))
+    assert ok, (fmt, kind, worst)
