@@ -22,44 +22,63 @@
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kAcc16 = 8;   // independent 16x16 accumulators per wave
 constexpr int kAcc32 = 4;   // independent 32x32 accumulators per wave
 
+// The MFMAs are inline asm with each accumulator tied to its own AGPR tuple:
+// with the builtins the register allocator shuffles accumulators between
+// tuples inside the loop (v_accvgpr moves), which is not the instruction's
+// rate.  Operands are written long before the loop; the accumulators are read
+// after 64 wait states.
 template <bool BIG>
 __global__ __launch_bounds__(256, 1) void fp4_stream(const uint32_t* __restrict__ bits, float* __restrict__ out,
                                                       int iters) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const uint32_t* p = bits + (t & 1023) * 16;
-  v8i a = {static_cast<int>(p[0]), static_cast<int>(p[1]), static_cast<int>(p[2]), static_cast<int>(p[3]), 0, 0, 0, 0};
-  v8i b = {static_cast<int>(p[4]), static_cast<int>(p[5]), static_cast<int>(p[6]), static_cast<int>(p[7]), 0, 0, 0, 0};
+  v4i a = {static_cast<int>(p[0]), static_cast<int>(p[1]), static_cast<int>(p[2]), static_cast<int>(p[3])};
+  v4i b = {static_cast<int>(p[4]), static_cast<int>(p[5]), static_cast<int>(p[6]), static_cast<int>(p[7])};
   const int sa = static_cast<int>(p[8] & 0x7f7f7f7fu) | 0x40404040, sb = static_cast<int>(p[9] & 0x7f7f7f7fu) | 0x40404040;
   float sum = 0.0f;
+  asm volatile("s_nop 7" ::: "memory");
   if constexpr (!BIG) {
     v4f acc[kAcc16];
 #pragma unroll
-    for (int i = 0; i < kAcc16; ++i) acc[i] = v4f{static_cast<float>(i), 0.f, 0.f, 0.f};   // distinct, never merged
-    for (int it = 0; it < iters; ++it) {
+    for (int i = 0; i < kAcc16; ++i) {
+      acc[i] = v4f{static_cast<float>(i), 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(acc[i]));
+    }
+    asm volatile("s_nop 7" ::: "memory");
+    int it = 0;
+    do {
 #pragma unroll
       for (int i = 0; i < kAcc16; ++i)
-        acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i], 4, 4, 0, sa, 0, sb);
-    }
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+a"(acc[i]) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    } while (++it < iters);
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
     for (int i = 0; i < kAcc16; ++i) sum += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
   } else {
     v16f acc[kAcc32];
 #pragma unroll
-    for (int i = 0; i < kAcc32; ++i)
+    for (int i = 0; i < kAcc32; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][e] = e ? 0.0f : static_cast<float>(i);
-    for (int it = 0; it < iters; ++it) {
+      asm volatile("" : "+a"(acc[i]));
+    }
+    asm volatile("s_nop 7" ::: "memory");
+    int it = 0;
+    do {
 #pragma unroll
       for (int i = 0; i < kAcc32; ++i)
-        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i], 4, 4, 0, sa, 0, sb);
-    }
+        asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+a"(acc[i]) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+    } while (++it < iters);
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
     for (int i = 0; i < kAcc32; ++i)
 #pragma unroll
@@ -105,6 +124,45 @@ __global__ __launch_bounds__(256) void f32_stream(const float* __restrict__ src,
   out[t] = sum;
 }
 
+// HBM read rates of two access patterns over the same bytes (rows x row_bytes,
+// row_bytes a multiple of 512), each lane folding its loads into one word:
+//  * flat: each wave reads 4 KB contiguous pieces (one 1 KB load instruction
+//    after another), pieces dealt round-robin over the waves;
+//  * tiles: the transform step's pattern: a wave owns 128 contiguous bytes of
+//    every row (its two 32-channel bf16 spans) and walks 16-row tiles, one
+//    load instruction = 16 rows x 64 bytes, `depth` tiles in flight.
+__global__ __launch_bounds__(256) void read_flat(const uint4* __restrict__ src, size_t n16, uint32_t* __restrict__ out) {
+  const size_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6, waves = (gridDim.x * blockDim.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  uint32_t acc = 0;
+  for (size_t p = wave * 256; p < n16; p += waves * 256) {
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = p + i * 64 + lane < n16 ? src[p + i * 64 + lane] : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void read_tiles(const uint8_t* __restrict__ src, int rows, int row_bytes, int tiles_per_wave,
+                                                  uint32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, q = lane >> 4;
+  const int col = (blockIdx.x * 4 + wave) * 128;
+  uint32_t acc = 0;
+  if (col < row_bytes) {
+    const int t0 = blockIdx.y * tiles_per_wave;
+    for (int t = 0; t < tiles_per_wave; ++t) {
+      const int row = min((t0 + t) * 16 + j, rows - 1);
+      const uint8_t* p = src + static_cast<size_t>(row) * row_bytes + col + 16 * q;
+      const uint4 a = *reinterpret_cast<const uint4*>(p), b = *reinterpret_cast<const uint4*>(p + 64);
+      acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+    }
+  }
+  out[(blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x] = acc;
+}
+
 template <typename K, typename... A>
 int launch(K k, int blocks, void* stream, A... args) {
   hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), args...);
@@ -121,6 +179,21 @@ int wush_ceiling_fp4(int which, int blocks, int iters, const uint32_t* bits, flo
   if (blocks < 1 || iters < 1 || !bits || !out) return 1;
   return which ? launch(fp4_stream<true>, blocks, stream, bits, out, iters)
                : launch(fp4_stream<false>, blocks, stream, bits, out, iters);
+}
+
+// Read rates: pattern 0 = flat (grid of `blocks` workgroups), 1 = tiles
+// (tiles_per_wave 16-row tiles per wave).  out: enough uint32 for the grid.
+int wush_ceiling_read(int pattern, const void* src, int rows, int row_bytes, int blocks, int tiles_per_wave,
+                      uint32_t* out, void* stream) {
+  if (!src || !out || rows < 16 || row_bytes < 512 || row_bytes % 512) return 1;
+  if (pattern == 0)
+    return launch(read_flat, blocks, stream, static_cast<const uint4*>(src),
+                  static_cast<size_t>(rows) * row_bytes / 16, out);
+  if (tiles_per_wave < 1) return 1;
+  const int gy = (rows / 16 + tiles_per_wave - 1) / tiles_per_wave;
+  hipLaunchKernelGGL(read_tiles, dim3(row_bytes / 512, gy), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(src), rows, row_bytes, tiles_per_wave, out);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 // fp32 16x16x4 with nchain in {2, 8} chains and nvalu in {0, 4, 8} vector FMAs per step.

@@ -67,6 +67,8 @@ def parse():
                          "plane-ordered scale path")
     ap.add_argument("--shared", type=int, default=0, metavar="G",
                     help="wus/wush: share one matrix per group of nblk/G adjacent blocks (shared-transform variant)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="square_sweep: every format x transform in turn, one JSON line each, with the layer loss")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=16.0, help="target wall time of the oracle sample")
     ap.add_argument("--cpu-workers", type=int, default=0,
@@ -415,7 +417,7 @@ def main():
         cases = [(wl, make_weights(wl), make_activations(wl)) for wl in wls]
         # the oracle's timing forks worker processes, so it runs before anything touches the GPU
         cpu = None
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and not args.sweep:
             cpu = cpu_baseline(cases, fmt, kind, args.shared, args.cpu_seconds, host_workers(args.cpu_workers))
 
     import aware_block_transforms_amd as W
@@ -442,6 +444,9 @@ def main():
         return bench_build(args, W, torch)
     if args.workload == "mfma_ceiling":
         return bench_mfma_ceiling(args, torch)
+
+    if args.sweep:
+        return bench_sweep(args, W, torch, cases[0])
 
     layers = [Layer(wl, fmt, kind, args.rotate, W, torch, Wt, X, shared=args.shared,
                     planes=not args.row_major_scales) for wl, Wt, X in cases]
@@ -530,6 +535,58 @@ def main():
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
+
+
+def bench_sweep(args, W, torch, case):
+    """Every format x transform of one workload (the square sweep): one JSON line each.
+
+    Each line times the step as the main bench does (transform+quantize, then
+    the matmul, rotated buffers) and reports the layer loss of the pages'
+    problem statement, sum((Yhat - W^T X)^2) / (d_out n), computed on the GPU by
+    wush_layer_loss against W^T X taken in fp64 on the host (numpy) from the same
+    seeded W and X.
+    """
+    wl, Wt, X = case
+    t0 = time.time()
+    Yref = (X.astype(np.float64) @ Wt.astype(np.float64).T).astype(np.float32)
+    ref_s = time.time() - t0
+    Yref_d = torch.from_numpy(Yref).cuda()
+    del Yref
+    lws = torch.empty(max(8, W.wush_loss_ws_bytes(wl.n, wl.d_out)) // 8, dtype=torch.float64, device="cuda")
+    loss = torch.empty(1, dtype=torch.float64, device="cuda")
+    results = []
+    for fmt in wl.formats:
+        for kind in wl.kinds:
+            L = Layer(wl, fmt, kind, args.rotate, W, torch, Wt, X)
+            ms_step, tq_ms, gm_ms = run_layer_steps([L], W, torch, args.steps, args.warmup, args.rotate)
+            W.wush_layer_loss(L.Y, Yref_d, loss, lws)
+            torch.cuda.synchronize()
+            flops = L.gemm_flops()
+            gm_t, tq_t = gm_ms[0] / 1e3, tq_ms[0] / 1e3
+            bound, peak = tq_engine(L)
+            t_alu = L.tq_flops() / (peak * 1e12)
+            gemm_peak = {"mxfp4": MXFP4_TFLOPS, "nvfp4": FP16_TFLOPS, "int4": INT8_TOPS}[fmt]
+            line = {"metric": METRIC, "value": round(flops / (ms_step / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+                    "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": fmt,
+                    "data": "synthetic",
+                    "config": {"workload": wl.name, "transform": kind, "format": fmt, "x_dtype": wl.dtype,
+                               "tokens": wl.n, "mx_scale_layout": "planes" if L.planes else "row-major"},
+                    "layer_loss": loss.item(),
+                    "tq_us": round(tq_t * 1e6, 2), "gemm_us": round(gm_t * 1e6, 2),
+                    "quant_GBps": round(L.tq_bytes() / tq_t / 1e9, 1),
+                    "tq_hbm_frac": round(L.tq_bytes() / tq_t / 1e9 / HBM_GBPS, 4),
+                    "tq_engine_frac": round(t_alu / tq_t, 4) if t_alu else None,
+                    "gemm_frac": round(flops / gm_t / 1e12 / gemm_peak, 4), "gemm_peak": gemm_peak}
+            if fmt == "int4":
+                rescale = INT4_RESCALE_OPS * L.M * L.N * (L.K // 32) / gm_t / 1e12
+                line["gemm_rescale_frac"] = round(rescale / VALU_TOPS, 4)
+            print(json.dumps(line), flush=True)
+            results.append((fmt, kind, loss.item()))
+            del L
+            torch.cuda.empty_cache()
+    print(json.dumps({"sweep_losses": {f"{f}/{k}": v for f, k, v in results}, "reference_s": round(ref_s, 1)}),
+          flush=True)
 
 
 def bench_had256(args, W, torch):
@@ -708,6 +765,26 @@ def bench_mfma_ceiling(args, torch):
             res[key + "_us"] = round(t * 1e6, 1)
             if nchain:
                 res[key + "_TFLOPs"] = round(cus * 4 * wps * it32 * nchain * 8 * 2048 / t / 1e12, 1)
+    # HBM read rate of the transform step's tile pattern against flat reads of
+    # the same bytes (the Qwen3-14B down-projection's bf16 activations)
+    lib.wush_ceiling_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    rows, row_bytes = 16384, 17408 * 2
+    nbuf = 3
+    bufs = [torch.empty(rows * row_bytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    for b in bufs:
+        b.fill_(1)
+    rout = torch.empty(16 << 20, dtype=torch.int32, device="cuda")
+    for pattern, name, blocks, tpw in ((0, "flat", cus * 8, 0), (1, "tiles_upw16", 0, 16), (1, "tiles_upw64", 0, 64)):
+        state = {"i": 0}
+
+        def run(p=pattern, bl=blocks, t=tpw, st=state):
+            b = bufs[st["i"] % nbuf]
+            st["i"] += 1
+            assert lib.wush_ceiling_read(p, b.data_ptr(), rows, row_bytes, bl, t, rout.data_ptr(), sp) == 0
+        t = timed(run)
+        res[f"read_{name}_GBps"] = round(rows * row_bytes / t / 1e9, 1)
+    del bufs
     v = res["fp4_16x16x128_random_TFLOPs"]
     print(json.dumps({"metric": "matrix-core ceiling, operands in registers", "value": v, "unit": "TFLOP/s",
                       "n_gpus": 1, "steps": 5, "warmup": 1, "ms_per_step": None, "higher_is_better": True,
