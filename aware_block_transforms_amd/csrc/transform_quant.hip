@@ -44,6 +44,20 @@ enum Fmt { kMX = 0, kNV = 1, kI4 = 2, kAmax = 3, kApply = 4, kMXP = 5 };
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Bit pattern of max |y[k]|: gfx950's v_maximum3_f32 with |.| source modifiers,
+// three values per instruction.  It is the IEEE 754-2019 maximum, so a NaN
+// anywhere propagates, and the result's bits order like the integer maximum of
+// the |y| bit patterns: equal for finite and infinite values (subnormals kept,
+// -0 and +0 both give 0), and at least 0x7f800001 when a NaN is present, which
+// is all the block quantizers read from it.
+template <int N>
+__device__ __forceinline__ uint32_t abs_max_bits(const float* y) {
+  float m = fabsf(y[0]);
+#pragma unroll
+  for (int k = 1; k < N; ++k) m = __builtin_elementwise_maximum(m, fabsf(y[k]));
+  return __float_as_uint(m);
+}
+
 // E2M1 code: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, exact ties to the even
 // code, saturating, sign bit copied.  Counts the decision thresholds passed.
 __device__ __forceinline__ uint32_t e2m1_code(float v) {
@@ -139,10 +153,12 @@ __device__ __forceinline__ BlockQuant<FMT> block_quant(uint32_t ab, float g) {
   BlockQuant<FMT> q{1.0f, 1.0f, 0u, false, false};
   const bool bad = ab >= 0x7f800000u;          // NaN or Inf in the block
   if constexpr (FMT == kMX) {
-    const uint32_t ex = ab >> 23;
-    const uint32_t sbyte = ex > 2u ? ex - 2u : 0u;             // e + 127
+    // 2^e = 2^(floor(log2 amax) - 2) as fp32 bits, the exponent field lowered by
+    // 2 and clamped at 0 (one saturating subtract); its field is the E8M0 byte
+    const uint32_t dbits = __builtin_elementwise_sub_sat(ab & 0x7f800000u, 0x01000000u);
+    const uint32_t sbyte = dbits >> 23;                        // e + 127
     q.mul = __uint_as_float((254u - sbyte) << 23);             // 2^-e
-    q.div = __uint_as_float(sbyte << 23);                      // 2^e, the E8M0 byte as exponent field
+    q.div = __uint_as_float(dbits);                            // 2^e, applied by the conversion
     q.zero = bad;
     q.scale = bad ? 0xffu : sbyte;
   } else if constexpr (FMT == kNV) {
@@ -230,9 +246,7 @@ template <int BS, int FMT>
 __device__ __forceinline__ void encode_store(const float (&y)[BS], size_t row, int blk, int nblk, int d_in, float g,
                                              uint8_t* __restrict__ codes, void* __restrict__ scales,
                                              uint32_t& run_max) {
-  uint32_t ab = 0;
-#pragma unroll
-  for (int k = 0; k < BS; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
+  const uint32_t ab = abs_max_bits<BS>(y);
   if constexpr (FMT == kAmax) {
     run_max = max(run_max, ab);
     return;
@@ -317,9 +331,14 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves
 // Block maximum: over the lane's values, then over its token's four lane
 // groups with two lane swaps; then the pinned block quantizers.
 //
-// Tokens past n re-read row n - 1 and rewrite its bytes unchanged; spans (and
-// at bs 16 blocks) past d_in repeat the last block the same way, so every
-// load and store stays inside the caller's buffers.
+// Addressing: every load and store of a unit goes through a buffer resource
+// whose base is the unit's first row (wave-uniform, in scalar registers) and
+// whose size ends at the unit's last token inside [0, n); the lane's part is a
+// 32-bit offset fixed for the whole run.  Tokens past n therefore read zeros
+// and their stores are dropped by the resource's range check.  Plane-ordered
+// scales interleave rows, so their stores carry a lane predicate instead.
+// Spans (and at bs 16 blocks) past d_in repeat the last block, rewriting its
+// bytes unchanged.  Every access stays inside the caller's buffers.
 constexpr int kSpans = 2;    // 32-channel spans per wave
 constexpr int kDepth = 4;    // units of x in flight ahead of the one computed
 
@@ -350,6 +369,21 @@ __device__ __forceinline__ uint32_t max_groups(uint32_t v) {
   return max(t[0], t[1]);
 }
 
+// Maxima of two values over a token's four lane groups at once: on return
+// every lane holds a's maximum in ma and b's in mb.  The first swap pairs rows
+// (a0 b0 a2 b2 | a1 b1 a3 b3), the second folds rows 2-3 onto 0-1 (A B A B),
+// the third spreads A and B over all four rows: three swaps and two maxima
+// instead of four and four.
+__device__ __forceinline__ void max_groups2(uint32_t a, uint32_t b, uint32_t& ma, uint32_t& mb) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  const uint32_t m = max(r[0], r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  const uint32_t mm = max(t[0], t[1]);
+  const auto u = __builtin_amdgcn_permlane16_swap(mm, mm, false, false);
+  ma = u[0];
+  mb = u[1];
+}
+
 // First element of lane group q's eight in its token row, for span sp.
 template <int BS>
 __device__ __forceinline__ int span_col(int sp, int q, int nblk) {
@@ -362,34 +396,90 @@ struct XRaw {
   static constexpr int kDwords = BF16 ? 4 : 8;
 };
 
-// Rows of one unit: the unit (clamped to the last one that holds tokens) and
-// lane j's row within it (clamped to n - 1).  row0 is wave-uniform, so every
-// address below is a uniform 64-bit base plus a 32-bit lane offset.
-struct UnitRows {
-  size_t row0;   // first token of the unit
-  int jj;        // this lane's token, relative to row0
-};
-__device__ __forceinline__ UnitRows unit_rows(int unit, int n, int j) {
-  const int ue = min(unit, (n - 1) >> 4);
-  return UnitRows{static_cast<size_t>(ue) * 16, min(j, n - 1 - ue * 16)};
+// Raw, unswizzled buffer resource of `bytes` bytes at `base` (dword 3 selects
+// the 32-bit data format untyped accesses need on CDNA).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
 }
 
-// Raw x of one span: elements col .. col + 7 of lane row jj of the unit at row0.
+// One unit: its first token and how many of its 16 tokens lie inside [0, n)
+// (0 past the end).  Both are wave-uniform.
+struct Unit {
+  size_t row0;
+  uint32_t rows;
+};
+__device__ __forceinline__ Unit unit_at(int unit, int n) {
+  // 32-bit unsigned arithmetic, so that it stays on the scalar unit
+  const uint32_t r0 = static_cast<uint32_t>(unit) * 16u, nn = static_cast<uint32_t>(n);
+  return Unit{static_cast<size_t>(r0), r0 >= nn ? 0u : min(nn - r0, 16u)};
+}
+
+// The unit's rows of an array of `row_bytes`-byte rows, as a buffer resource.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void* base, const Unit& un, uint32_t row_bytes) {
+  return buf_rsrc(static_cast<const uint8_t*>(base) + un.row0 * row_bytes, un.rows * row_bytes);
+}
+
+// Raw x of one span of a unit: the lane's 16 (fp32: 32) bytes at offset xoff
+// of the unit's rows (its token's elements col .. col + 7).
 template <bool BF16>
-__device__ __forceinline__ void load_x(const void* X, const UnitRows& ur, int d_in, int col,
+__device__ __forceinline__ void load_x(const void* X, const Unit& un, uint32_t row_bytes, uint32_t xoff,
                                        uint32_t (&raw)[XRaw<BF16>::kDwords]) {
-  const uint32_t off = static_cast<uint32_t>(ur.jj * d_in + col);
-  if constexpr (BF16) {
-    const uint16_t* base = reinterpret_cast<const uint16_t*>(X) + ur.row0 * d_in;
-    const uint4 v = *reinterpret_cast<const uint4*>(base + off);
-    raw[0] = v.x; raw[1] = v.y; raw[2] = v.z; raw[3] = v.w;
-  } else {
-    const float* base = reinterpret_cast<const float*>(X) + ur.row0 * d_in;
-    const uint4* p = reinterpret_cast<const uint4*>(base + off);
-    const uint4 a = p[0], b = p[1];
-    raw[0] = a.x; raw[1] = a.y; raw[2] = a.z; raw[3] = a.w;
-    raw[4] = b.x; raw[5] = b.y; raw[6] = b.z; raw[7] = b.w;
+  const __amdgpu_buffer_rsrc_t r = unit_rsrc(X, un, row_bytes);
+  const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, xoff, 0, 0));
+  raw[0] = v.x; raw[1] = v.y; raw[2] = v.z; raw[3] = v.w;
+  if constexpr (!BF16) {
+    const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, xoff + 16, 0, 0));
+    raw[4] = w.x; raw[5] = w.y; raw[6] = w.z; raw[7] = w.w;
   }
+}
+
+// Stores through a unit's resource: lane offset v plus wave-uniform offset s.
+__device__ __forceinline__ void st_b8(uint32_t x, __amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(x), r, v, s, 0);
+}
+__device__ __forceinline__ void st_b16(uint32_t x, __amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(x), r, v, s, 0);
+}
+__device__ __forceinline__ void st_b32(uint32_t x, __amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  __builtin_amdgcn_raw_buffer_store_b32(x, r, v, s, 0);
+}
+__device__ __forceinline__ void st_b64(uint32_t x, uint32_t y, __amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(v2u{x, y}, r, v, s, 0);
+}
+__device__ __forceinline__ void st_f4(float a, float b, float c, float d, __amdgpu_buffer_rsrc_t r, uint32_t v,
+                                      uint32_t s) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(v4u{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c),
+                                             __float_as_uint(d)},
+                                         r, v, s, 0);
+}
+
+// Scale of (lane's token, block b) in the row-major scale array of a unit.
+template <int FMT>
+__device__ __forceinline__ void store_unit_scale(void* scales, const Unit& un, int nblk, int j, int b, uint32_t sc) {
+  constexpr uint32_t ssz = FMT == kI4 ? 2u : 1u;
+  const __amdgpu_buffer_rsrc_t r = unit_rsrc(scales, un, static_cast<uint32_t>(nblk) * ssz);
+  if constexpr (FMT == kI4)
+    st_b16(sc, r, static_cast<uint32_t>(j * nblk) * ssz, static_cast<uint32_t>(b) * ssz);
+  else
+    st_b8(sc, r, static_cast<uint32_t>(j * nblk), static_cast<uint32_t>(b));
+}
+
+// Plane-ordered scale of (lane's token, block 8 kb + bl), the layout of
+// mxfp4_plane_offset: every row of a unit lies in one 256-row tile at one tile
+// position, so the (tile, K block) region is a wave-uniform 2 KB base, and the
+// lane adds plane bl's 256 bytes, 16 per token and the position rotated in odd
+// planes.  kb must be wave-uniform.  Tokens past n (the last tile's planes hold
+// rows past n) get an offset outside the 2 KB, which the range check drops.
+__device__ __forceinline__ void store_plane_scale(void* scales, const Unit& un, int nblk, int j, int kb, int bl,
+                                                  uint32_t sc) {
+  const uint32_t r = static_cast<uint32_t>(un.row0) & 255u;
+  const uint8_t* base = static_cast<const uint8_t*>(scales) + ((un.row0 >> 8) * static_cast<size_t>(nblk / 8) + kb) * 2048;
+  const uint32_t pos0 = 8u * (r >> 7) + ((r >> 4) & 7u);
+  const uint32_t off = static_cast<uint32_t>(bl) * 256u + 16u * static_cast<uint32_t>(j) + (pos0 ^ (8u * (bl & 1)));
+  st_b8(sc, buf_rsrc(base, 2048u), static_cast<uint32_t>(j) < un.rows ? off : 0x80000000u, 0u);
 }
 
 // x operands of the eight MFMA steps of one span for lane (g, j).
@@ -479,12 +569,9 @@ __device__ __forceinline__ void t_steps(const TRaw& tr, float (&ta)[2][8]) {
 
 // The MFMA chains, block maxima, encoders and stores of one span of one unit.
 template <int BS, int FMT>
-__device__ __forceinline__ void span_unit(const float (&ta)[2][8], const float (&xv)[8], int sp, int nblk, int q,
-                                          const UnitRows& ur, int d_in, float g, uint8_t* __restrict__ codes,
+__device__ __forceinline__ void span_unit(const float (&ta)[2][8], const float (&xv)[8], int sp, int nblk, int q, int j,
+                                          const Unit& un, int d_in, float g, uint8_t* __restrict__ codes,
                                           void* __restrict__ scales, uint32_t& run_max) {
-  const int jj = ur.jj;
-  uint8_t* const cbase = codes + ur.row0 * (d_in / 2);                       // code rows of the unit
-  const int crow = jj * (d_in / 2);
   v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
   if constexpr (BS == 32) {
 #pragma unroll
@@ -498,35 +585,32 @@ __device__ __forceinline__ void span_unit(const float (&ta)[2][8], const float (
       for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[h][c], xv[4 * h + c], acc[h], 0, 0, 0);
   }
   constexpr int QF = FMT == kMXP ? kMX : FMT;
+  const uint32_t code_row = static_cast<uint32_t>(d_in / 2);
   if constexpr (BS == 32) {
     const int b = min(sp, nblk - 1);
     float y[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) { y[e] = acc[0][e]; y[4 + e] = acc[1][e]; }
     if constexpr (FMT == kApply) {
-      float* dst = reinterpret_cast<float*>(codes) + ur.row0 * d_in + static_cast<uint32_t>(jj * d_in + b * 32 + 8 * q);
-      reinterpret_cast<float4*>(dst)[0] = make_float4(y[0], y[1], y[2], y[3]);
-      reinterpret_cast<float4*>(dst)[1] = make_float4(y[4], y[5], y[6], y[7]);
+      const __amdgpu_buffer_rsrc_t r = unit_rsrc(codes, un, static_cast<uint32_t>(d_in) * 4u);
+      const uint32_t v = static_cast<uint32_t>(j * d_in + 8 * q) * 4u, so = static_cast<uint32_t>(b) * 128u;
+      st_f4(y[0], y[1], y[2], y[3], r, v, so);
+      st_f4(y[4], y[5], y[6], y[7], r, v + 16u, so);
       return;
     }
-    uint32_t ab = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
-    ab = max_groups(ab);
+    const uint32_t ab = max_groups(abs_max_bits<8>(y));
     if constexpr (FMT == kAmax) {
       run_max = max(run_max, ab);
     } else {
       const BlockQuant<QF> bq = block_quant<QF>(ab, g);
       uint32_t w[1];
       encode_pairs<QF, 4>(y, bq, w);
-      *reinterpret_cast<uint32_t*>(cbase + static_cast<uint32_t>(crow + b * 16 + 4 * q)) = w[0];
-      if constexpr (FMT == kMXP) {
-        // every row of the unit shares its 256-row tile and plane position: lane row jj adds 16 jj
-        uint8_t* sbase = reinterpret_cast<uint8_t*>(scales) + mxfp4_plane_offset(static_cast<int>(ur.row0), b, nblk / 8);
-        sbase[static_cast<uint32_t>(16 * jj)] = static_cast<uint8_t>(bq.scale);
-      } else {
-        store_scale<QF>(scales, ur.row0 * nblk + static_cast<uint32_t>(jj * nblk + b), bq.scale);
-      }
+      st_b32(w[0], unit_rsrc(codes, un, code_row), static_cast<uint32_t>(j) * code_row + 4u * q,
+             static_cast<uint32_t>(b) * 16u);
+      if constexpr (FMT == kMXP)
+        store_plane_scale(scales, un, nblk, j, b >> 3, b & 7, bq.scale);
+      else
+        store_unit_scale<QF>(scales, un, nblk, j, b, bq.scale);
     }
   } else {
 #pragma unroll
@@ -534,22 +618,20 @@ __device__ __forceinline__ void span_unit(const float (&ta)[2][8], const float (
       const int b = min(2 * sp + h, nblk - 1);
       float y[4] = {acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
       if constexpr (FMT == kApply) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(codes) + ur.row0 * d_in +
-                                   static_cast<uint32_t>(jj * d_in + b * 16 + 4 * q)) = make_float4(y[0], y[1], y[2], y[3]);
+        st_f4(y[0], y[1], y[2], y[3], unit_rsrc(codes, un, static_cast<uint32_t>(d_in) * 4u),
+              static_cast<uint32_t>(j * d_in + 4 * q) * 4u, static_cast<uint32_t>(b) * 64u);
         continue;
       }
-      uint32_t ab = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
-      ab = max_groups(ab);
+      const uint32_t ab = max_groups(abs_max_bits<4>(y));
       if constexpr (FMT == kAmax) {
         run_max = max(run_max, ab);
       } else {
         const BlockQuant<QF> bq = block_quant<QF>(ab, g);
         uint32_t w[1];
         encode_pairs<QF, 2>(y, bq, w);
-        *reinterpret_cast<uint16_t*>(cbase + static_cast<uint32_t>(crow + b * 8 + 2 * q)) = static_cast<uint16_t>(w[0]);
-        store_scale<QF>(scales, ur.row0 * nblk + static_cast<uint32_t>(jj * nblk + b), bq.scale);
+        st_b16(w[0], unit_rsrc(codes, un, code_row), static_cast<uint32_t>(j) * code_row + 2u * q,
+               static_cast<uint32_t>(b) * 8u);
+        store_unit_scale<QF>(scales, un, nblk, j, b, bq.scale);
       }
     }
   }
@@ -563,10 +645,10 @@ __device__ __forceinline__ void span_unit(const float (&ta)[2][8], const float (
 // writing block b0's and groups 1 and 3 block b0 + 1's.
 template <int FMT>
 __device__ __forceinline__ void pair_unit(const float (&ta)[2][2][8], const float (&xv)[2][8], int b0, int nblk, int q,
-                                          const UnitRows& ur, int d_in, float g, uint8_t* __restrict__ codes,
+                                          int j, const Unit& un, int d_in, float g, uint8_t* __restrict__ codes,
                                           void* __restrict__ scales) {
   constexpr int QF = FMT == kMXP ? kMX : FMT;
-  uint32_t w[2], sc[2];
+  float y[2][8];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
@@ -575,31 +657,31 @@ __device__ __forceinline__ void pair_unit(const float (&ta)[2][2][8], const floa
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[s][h][c], xv[s][c], acc[h], 0, 0, 0);
-    float y[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { y[e] = acc[0][e]; y[4 + e] = acc[1][e]; }
-    uint32_t ab = 0;
+    for (int e = 0; e < 4; ++e) { y[s][e] = acc[0][e]; y[s][4 + e] = acc[1][e]; }
+  }
+  uint32_t ab[2];
+  max_groups2(abs_max_bits<8>(y[0]), abs_max_bits<8>(y[1]), ab[0], ab[1]);
+  uint32_t w[2], sc[2];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ab = max(ab, __float_as_uint(y[k]) & 0x7fffffffu);
-    ab = max_groups(ab);
-    const BlockQuant<QF> bq = block_quant<QF>(ab, g);
+  for (int s = 0; s < 2; ++s) {
+    const BlockQuant<QF> bq = block_quant<QF>(ab[s], g);
     uint32_t ws[1];
-    encode_pairs<QF, 4>(y, bq, ws);
+    encode_pairs<QF, 4>(y[s], bq, ws);
     w[s] = ws[0];
     sc[s] = bq.scale;
   }
   swap32(w[0], w[1]);
   swap16(w[0], w[1]);
-  *reinterpret_cast<uint2*>(codes + ur.row0 * (d_in / 2) + static_cast<uint32_t>(ur.jj * (d_in / 2) + b0 * 16 + 8 * q)) =
-      make_uint2(w[0], w[1]);
+  const uint32_t code_row = static_cast<uint32_t>(d_in / 2);
+  st_b64(w[0], w[1], unit_rsrc(codes, un, code_row), static_cast<uint32_t>(j) * code_row + 8u * q,
+         static_cast<uint32_t>(b0) * 16u);
   const int odd = q & 1;
   const uint32_t scale = odd ? sc[1] : sc[0];
-  if constexpr (FMT == kMXP) {
-    uint8_t* sbase = reinterpret_cast<uint8_t*>(scales) + mxfp4_plane_offset(static_cast<int>(ur.row0), b0 + odd, nblk / 8);
-    sbase[static_cast<uint32_t>(16 * ur.jj)] = static_cast<uint8_t>(scale);
-  } else {
-    store_scale<QF>(scales, ur.row0 * nblk + static_cast<uint32_t>(ur.jj * nblk + b0 + odd), scale);
-  }
+  if constexpr (FMT == kMXP)   // b0 is even: both blocks share their 256-wide K block
+    store_plane_scale(scales, un, nblk, j, b0 >> 3, (b0 & 7) + odd, scale);
+  else
+    store_unit_scale<QF>(scales, un, nblk, j, b0 + odd, scale);
 }
 
 // Does the merged-store pair path apply?  bs 32, a quantized format, and an
@@ -610,15 +692,15 @@ constexpr bool pair_format(int bs, int fmt) { return bs == 32 && (fmt == kMX || 
 // One unit of all the wave's spans: merged stores (PAIR), else span by span.
 template <int BS, int FMT, bool PAIR>
 __device__ __forceinline__ void unit_out(const float (&ta)[kSpans][2][8], const float (&xv)[kSpans][8], int sp0,
-                                         int nblk, int q, const UnitRows& ur, int d_in, float g,
+                                         int nblk, int q, int j, const Unit& un, int d_in, float g,
                                          uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t& run_max) {
   if constexpr (PAIR) {
     static_assert(kSpans == 2 && pair_format(BS, FMT), "pair path: two bs-32 spans of a quantized format");
-    pair_unit<FMT>(ta, xv, sp0, nblk, q, ur, d_in, g, codes, scales);
+    pair_unit<FMT>(ta, xv, sp0, nblk, q, j, un, d_in, g, codes, scales);
   } else {
 #pragma unroll
     for (int s = 0; s < kSpans; ++s)
-      span_unit<BS, FMT>(ta[s], xv[s], sp0 + s, nblk, q, ur, d_in, g, codes, scales, run_max);
+      span_unit<BS, FMT>(ta[s], xv[s], sp0 + s, nblk, q, j, un, d_in, g, codes, scales, run_max);
   }
 }
 
@@ -637,9 +719,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
   const int sp0 = (blockIdx.x * kWavesPerGroup + wave) * kSpans;
   if (sp0 >= nspans) return;                      // wave-uniform; no barrier follows
   const int u0 = blockIdx.y * upw;                // first unit (16 tokens) of this wave
-  int col[kSpans];
+  // the lane's byte offset within a unit's rows, per span (fixed for the run)
+  constexpr uint32_t kEsz = BF16 ? 2u : 4u;
+  const uint32_t row_bytes = static_cast<uint32_t>(d_in) * kEsz;
+  uint32_t xoff[kSpans];
 #pragma unroll
-  for (int s = 0; s < kSpans; ++s) col[s] = span_col<BS>(sp0 + s, q, nblk);
+  for (int s = 0; s < kSpans; ++s) xoff[s] = static_cast<uint32_t>(j * d_in + span_col<BS>(sp0 + s, q, nblk)) * kEsz;
   // T's loads first, then the first units of x; the wait for T (from L2)
   // then leaves the loads of x (from HBM) in flight
   TRaw traw[kSpans];
@@ -649,9 +734,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
   uint32_t raw[kDepth][kSpans][R];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
-    const UnitRows ur = unit_rows(u0 + d, n, j);
+    const Unit un = unit_at(u0 + d, n);
 #pragma unroll
-    for (int s = 0; s < kSpans; ++s) load_x<BF16>(X, ur, d_in, col[s], raw[d][s]);
+    for (int s = 0; s < kSpans; ++s) load_x<BF16>(X, un, row_bytes, xoff[s], raw[d][s]);
   }
   __builtin_amdgcn_sched_barrier(0);
   float ta[kSpans][2][8];
@@ -669,12 +754,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
 #pragma unroll
       for (int s = 0; s < kSpans; ++s) x_steps<BF16>(raw[d][s], xv[s]);
       __builtin_amdgcn_sched_barrier(0);
-      const UnitRows un = unit_rows(u0 + u + d + kDepth, n, j);
+      const Unit nx = unit_at(u0 + u + d + kDepth, n);
 #pragma unroll
-      for (int s = 0; s < kSpans; ++s) load_x<BF16>(X, un, d_in, col[s], raw[d][s]);
+      for (int s = 0; s < kSpans; ++s) load_x<BF16>(X, nx, row_bytes, xoff[s], raw[d][s]);
       __builtin_amdgcn_sched_barrier(0);
-      const UnitRows ur = unit_rows(u0 + u + d, n, j);
-      unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, ur, d_in, g, codes, scales, run_max);
+      unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, j, unit_at(u0 + u + d, n), d_in, g, codes, scales, run_max);
     }
   }
 #pragma unroll
@@ -682,8 +766,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
     float xv[kSpans][8];
 #pragma unroll
     for (int s = 0; s < kSpans; ++s) x_steps<BF16>(raw[d][s], xv[s]);
-    const UnitRows ur = unit_rows(u0 + u + d, n, j);
-    unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, ur, d_in, g, codes, scales, run_max);
+    unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, j, unit_at(u0 + u + d, n), d_in, g, codes, scales, run_max);
   }
   if constexpr (FMT == kAmax) {
 #pragma unroll
