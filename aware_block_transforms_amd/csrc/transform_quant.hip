@@ -689,6 +689,17 @@ __device__ __forceinline__ void pair_unit(const float (&ta)[2][2][8], const floa
 // pair of 2-byte scales is aligned).
 constexpr bool pair_format(int bs, int fmt) { return bs == 32 && (fmt == kMX || fmt == kI4 || fmt == kMXP); }
 
+// Vector-memory stores one unit issues (for the prologue above).
+template <int BS, int FMT, bool PAIR>
+constexpr int stores_per_unit() {
+  if constexpr (FMT == kAmax) return 0;
+  else if constexpr (PAIR) return 2;                        // codes of both blocks, one scale
+  else if constexpr (FMT == kApply) return kSpans * 2;      // two float4 per span (bs 16: one per block)
+  else if constexpr (BS == 32) return kSpans * 2;           // codes and scale per span
+  else return kSpans * 4;                                   // codes and scale per block, two blocks per span
+}
+constexpr bool kMatchEntry = true;
+
 // One unit of all the wave's spans: merged stores (PAIR), else span by span.
 template <int BS, int FMT, bool PAIR>
 __device__ __forceinline__ void unit_out(const float (&ta)[kSpans][2][8], const float (&xv)[kSpans][8], int sp0,
@@ -732,11 +743,24 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
   for (int s = 0; s < kSpans; ++s) load_t<BS>(T, tmap, ngroups, sp0 + s, nblk, q, j, traw[s]);
   __builtin_amdgcn_sched_barrier(0);
   uint32_t raw[kDepth][kSpans][R];
+  // Loads and stores retire through one in-order counter, and the loop's
+  // waits are shared by all its iterations: each unit's loads are followed by
+  // the previous unit's stores in the loop, so here each unit's loads are
+  // followed by as many stores that write nothing (a resource of size 0).
+  // The compiler then sees the same count of later operations before every
+  // wait for a unit's loads, on entry and in steady state, and waits for that
+  // unit's loads only, not for the units after it and the stores between.
+  const __amdgpu_buffer_rsrc_t nowhere = buf_rsrc(codes, 0u);
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
     const Unit un = unit_at(u0 + d, n);
 #pragma unroll
     for (int s = 0; s < kSpans; ++s) load_x<BF16>(X, un, row_bytes, xoff[s], raw[d][s]);
+    if constexpr (kMatchEntry) {
+#pragma unroll
+      for (int k = 0; k < stores_per_unit<BS, FMT, PAIR>(); ++k) st_b32(0u, nowhere, 256u * (kDepth * d + k), 0u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   float ta[kSpans][2][8];
