@@ -684,10 +684,87 @@ __device__ __forceinline__ void pair_unit(const float (&ta)[2][2][8], const floa
     store_unit_scale<QF>(scales, un, nblk, j, b0 + odd, scale);
 }
 
-// Does the merged-store pair path apply?  bs 32, a quantized format, and an
-// even number of blocks (so every wave's two blocks lie inside d_in and a
-// pair of 2-byte scales is aligned).
-constexpr bool pair_format(int bs, int fmt) { return bs == 32 && (fmt == kMX || fmt == kI4 || fmt == kMXP); }
+// Every lane receives the value v of each of its token's four lane groups:
+// o[r] = v of lane group r (three lane swaps).
+__device__ __forceinline__ void gather_groups(uint32_t v, uint32_t (&o)[4]) {
+  const auto t = __builtin_amdgcn_permlane16_swap(v, v, false, false);     // rows: (v0 v0 v2 v2), (v1 v1 v3 v3)
+  const auto u = __builtin_amdgcn_permlane32_swap(t[0], t[0], false, false);
+  const auto w = __builtin_amdgcn_permlane32_swap(t[1], t[1], false, false);
+  o[0] = u[0];
+  o[1] = w[0];
+  o[2] = u[1];
+  o[3] = w[1];
+}
+
+// NVFP4 (bs 16): the four blocks of a unit's two spans (blocks 2 sp0 .. 2 sp0
+// + 3, all inside d_in), with the scale work split over the lane groups.  A
+// block's scale takes two correctly rounded divisions and the E4M3 rounding,
+// about forty vector instructions; every lane of a token would compute the
+// same four.  Instead the block maxima are reduced so that lane group r ends
+// with block r's (two swaps per pair of blocks, one more between the pairs),
+// each lane computes that one block's multiplier, scale and flags, and the
+// lanes gather the four multipliers and flags back (three swaps each).  The
+// 2-byte code pieces (lane group r holds bytes 2r, 2r+1 of every block) are
+// then transposed so that lane group r holds block r's 8 bytes: one 8-byte
+// code store and one scale store per lane.
+template <int FMT>
+__device__ __forceinline__ void quad_unit(const float (&ta)[2][2][8], const float (&xv)[2][8], int sp0, int nblk, int q,
+                                          int j, const Unit& un, int d_in, float g, uint8_t* __restrict__ codes,
+                                          void* __restrict__ scales) {
+  static_assert(FMT == kNV, "quad path: NVFP4");
+  float y[4][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[s][h][c], xv[s][4 * h + c], acc[h], 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[2 * s + h][e] = acc[h][e];
+  }
+  // maxima: after the pair swaps row r holds blocks (0, 1) or (2, 3) over two
+  // rows each; the swap between the row pairs folds them to block r in row r
+  const auto r01 = __builtin_amdgcn_permlane16_swap(abs_max_bits<4>(y[0]), abs_max_bits<4>(y[1]), false, false);
+  const auto r23 = __builtin_amdgcn_permlane16_swap(abs_max_bits<4>(y[2]), abs_max_bits<4>(y[3]), false, false);
+  const auto f = __builtin_amdgcn_permlane32_swap(max(r01[0], r01[1]), max(r23[0], r23[1]), false, false);
+  const BlockQuant<kNV> own = block_quant<kNV>(max(f[0], f[1]), g);
+  uint32_t mul[4], flg[4];
+  gather_groups(__float_as_uint(own.mul), mul);
+  gather_groups(own.scale | (own.zero ? 0x100u : 0u) | (own.soft ? 0x200u : 0u), flg);
+  uint32_t c16[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const BlockQuant<kNV> bq{__uint_as_float(mul[b]), 1.0f, flg[b] & 0xffu, (flg[b] & 0x100u) != 0u,
+                             (flg[b] & 0x200u) != 0u};
+    uint32_t w[1];
+    encode_pairs<kNV, 2>(y[b], bq, w);
+    c16[b] = w[0];
+  }
+  // 4 x 4 transpose of 2-byte pieces across the lane groups
+  uint32_t p0 = (c16[0] & 0xffffu) | (c16[1] << 16), p1 = (c16[2] & 0xffffu) | (c16[3] << 16);
+  swap32(p0, p1);                                           // rows 0-1: blocks 0, 1; rows 2-3: blocks 2, 3
+  uint32_t q0 = __builtin_amdgcn_perm(p1, p0, 0x05040100u); // low pieces of p0, p1
+  uint32_t q1 = __builtin_amdgcn_perm(p1, p0, 0x07060302u); // high pieces
+  swap16(q0, q1);
+  const uint32_t d0 = __builtin_amdgcn_perm(q1, q0, 0x05040100u);
+  const uint32_t d1 = __builtin_amdgcn_perm(q1, q0, 0x07060302u);
+  const uint32_t code_row = static_cast<uint32_t>(d_in / 2);
+  st_b64(d0, d1, unit_rsrc(codes, un, code_row), static_cast<uint32_t>(j) * code_row + 8u * q,
+         static_cast<uint32_t>(2 * sp0) * 8u);
+  store_unit_scale<kNV>(scales, un, nblk, j, 2 * sp0 + q, own.scale);
+}
+
+// Does the merged-store path apply?  bs 32 with an even number of blocks (two
+// blocks per wave, a pair of 2-byte scales aligned), or NVFP4 at bs 16 with a
+// multiple of four blocks (four per wave), so that every wave's blocks lie
+// inside d_in.
+constexpr bool pair_format(int bs, int fmt) {
+  return (bs == 32 && (fmt == kMX || fmt == kI4 || fmt == kMXP)) || (bs == 16 && fmt == kNV);
+}
 
 // Vector-memory stores one unit issues (for the prologue above).
 template <int BS, int FMT, bool PAIR>
@@ -706,8 +783,11 @@ __device__ __forceinline__ void unit_out(const float (&ta)[kSpans][2][8], const 
                                          int nblk, int q, int j, const Unit& un, int d_in, float g,
                                          uint8_t* __restrict__ codes, void* __restrict__ scales, uint32_t& run_max) {
   if constexpr (PAIR) {
-    static_assert(kSpans == 2 && pair_format(BS, FMT), "pair path: two bs-32 spans of a quantized format");
-    pair_unit<FMT>(ta, xv, sp0, nblk, q, j, un, d_in, g, codes, scales);
+    static_assert(kSpans == 2 && pair_format(BS, FMT), "merged stores: two spans of a quantized format");
+    if constexpr (BS == 32)
+      pair_unit<FMT>(ta, xv, sp0, nblk, q, j, un, d_in, g, codes, scales);
+    else
+      quad_unit<FMT>(ta, xv, sp0, nblk, q, j, un, d_in, g, codes, scales);
   } else {
 #pragma unroll
     for (int s = 0; s < kSpans; ++s)
@@ -886,7 +966,7 @@ DenseFn dense(bool bf16, bool pair) {
 }
 
 DenseFn select_dense(int fmt, int bs, bool bf16, int nblk) {
-  const bool pair = nblk % 2 == 0;
+  const bool pair = bs == 32 ? nblk % 2 == 0 : nblk % 4 == 0;
   if (bs == 32) {
     switch (fmt) {
       case kMX: return dense<32, kMX>(bf16, pair);

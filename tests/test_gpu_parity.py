@@ -18,7 +18,7 @@ from gpu_util import DEV, to_dev, x_dev, host, scales_np, gemm_close
 pytestmark = pytest.mark.gpu
 
 SHAPES32 = [(1, 32), (200, 160), (130, 544), (64, 256)]
-SHAPES16 = [(1, 16), (200, 208), (70, 48)]
+SHAPES16 = [(1, 16), (200, 208), (70, 48), (130, 256)]   # the last: four blocks per wave (NVFP4 merged stores)
 
 
 def _oracle_tq(fmt, kind, X, Wt):
