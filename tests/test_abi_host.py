@@ -413,3 +413,47 @@ def test_asm_mfma_operands_are_written_early():
     code = _kernel_code(_device_asm("gemm_nvfp4.hip"), "gemm_nvfp4_lds")
     assert sum(1 for l in code if l.startswith("v_mfma")) >= 64
     assert _asm_mfma_hazards(code) == []
+
+
+def _loop_bodies(code):
+    """Instruction lists of the innermost loops (a label followed later by a
+    backward branch to it, with no other label in between)."""
+    import re
+    loops = []
+    for i, line in enumerate(code):
+        m = re.match(r"^(\.LBB\w*):$", line)
+        if not m:
+            continue
+        body = []
+        for l in code[i + 1:]:
+            if re.match(r"^\.LBB\w*:$", l):
+                body = None
+                break
+            body.append(l)
+            if l.startswith("s_cbranch") and l.split()[-1] == m.group(1):
+                break
+        else:
+            body = None
+        if body:
+            loops.append(body)
+    return loops
+
+
+def test_transform_loop_waits_cover_one_unit():
+    """The streaming transform kernel keeps kDepth units of loads in flight
+    with each unit's stores between them; its prologue issues matching
+    stores into a zero-size resource so that every load wait in the loop
+    waits for one unit's loads only.  In the compiled MXFP4 plane-order kernel
+    (bf16, merged stores) every vmcnt wait of the main loop must therefore
+    allow the same, largest count; a regression to the prologue-only state
+    shows as smaller counts at the loop's first units."""
+    import re
+    code = _kernel_code(_device_asm("transform_quant.hip"), "tq_dense_kernelILi32ELi5ELb1ELb1E")
+    loops = [b for b in _loop_bodies(code) if sum(1 for l in b if l.startswith("v_mfma")) >= 64]
+    assert len(loops) == 1, len(loops)
+    waits = [int(m.group(1)) for l in loops[0] for m in [re.search(r"vmcnt\((\d+)\)", l)] if m]
+    loads = sum(1 for l in loops[0] if l.startswith("buffer_load"))
+    stores = sum(1 for l in loops[0] if l.startswith("buffer_store"))
+    assert loads == 8 and stores == 8, (loads, stores)
+    # each unit: its two loads, waited with 15 and 14 later operations pending
+    assert sorted(set(waits)) == [14, 15], waits
