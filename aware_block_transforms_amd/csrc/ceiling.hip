@@ -87,6 +87,48 @@ __global__ __launch_bounds__(256, 1) void fp4_stream(const uint32_t* __restrict_
   out[t] = sum;
 }
 
+// The same instruction with operands that change from one MFMA to the next, in
+// the W4A4 matmul's order: for each of 8 A operand sets, the 8 B sets into 8
+// accumulators (B changes every MFMA, A every eighth), each set with its own
+// random scale bytes.  A matmul feeds new operand bits to every MFMA, which
+// the repeated-operand stream above does not.
+__global__ __launch_bounds__(256, 1) void fp4_stream_vary(const uint32_t* __restrict__ bits, float* __restrict__ out,
+                                                         int iters) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  v4i a[8], b[8];
+  int sa[8], sb[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t* p = bits + ((t + 37 * c) & 1023) * 16;
+    const uint32_t* q = bits + ((t + 101 * c + 500) & 1023) * 16;
+    a[c] = v4i{static_cast<int>(p[0]), static_cast<int>(p[1]), static_cast<int>(p[2]), static_cast<int>(p[3])};
+    b[c] = v4i{static_cast<int>(q[4]), static_cast<int>(q[5]), static_cast<int>(q[6]), static_cast<int>(q[7])};
+    sa[c] = static_cast<int>(p[8] & 0x7f7f7f7fu) | 0x40404040;
+    sb[c] = static_cast<int>(q[9] & 0x7f7f7f7fu) | 0x40404040;
+  }
+  float sum = 0.0f;
+  v4f acc[kAcc16];
+#pragma unroll
+  for (int i = 0; i < kAcc16; ++i) {
+    acc[i] = v4f{static_cast<float>(i), 0.f, 0.f, 0.f};
+    asm volatile("" : "+a"(acc[i]));
+  }
+  asm volatile("s_nop 7" ::: "memory");
+  int it = 0;
+  do {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int i = 0; i < kAcc16; ++i)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+a"(acc[i]) : "v"(b[i]), "v"(a[q]), "v"(sb[i]), "v"(sa[q]));
+  } while (++it < iters);
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < kAcc16; ++i) sum += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  out[t] = sum;
+}
+
 // NCHAIN chains of 8 dependent fp32 16x16x4 MFMAs per iteration (the dense
 // transform's step pattern at bs 32), with NVALU independent vector FMAs
 // placed between them.
@@ -173,10 +215,12 @@ int launch(K k, int blocks, void* stream, A... args) {
 
 extern "C" {
 
-// which: 0 = 16x16x128, 1 = 32x32x64.  bits: >= 1024 * 16 uint32 of operand
+// which: 0 = 16x16x128, 1 = 32x32x64, 2 = 16x16x128 with operands that change
+// every MFMA (64 per iteration).  bits: >= 1024 * 16 uint32 of operand
 // bits; out: blocks * 256 floats.  Returns 0 on a successful launch.
 int wush_ceiling_fp4(int which, int blocks, int iters, const uint32_t* bits, float* out, void* stream) {
   if (blocks < 1 || iters < 1 || !bits || !out) return 1;
+  if (which == 2) return launch(fp4_stream_vary, blocks, stream, bits, out, iters);
   return which ? launch(fp4_stream<true>, blocks, stream, bits, out, iters)
                : launch(fp4_stream<false>, blocks, stream, bits, out, iters);
 }

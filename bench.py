@@ -714,7 +714,8 @@ def bench_mfma_ceiling(args, torch):
     """Matrix-core rates with operands in registers (libwush_ceiling.so).
 
     FP4 block-scaled MFMA streams (the W4A4 matmul's instruction) on random and
-    on zero operand bits, one wave per SIMD; fp32 16x16x4 MFMA (the dense
+    on zero operand bits, one wave per SIMD, and on random operands that change
+    every MFMA as in the matmul; fp32 16x16x4 MFMA (the dense
     transform's instruction) as 2 or 8 accumulation chains of 8 steps, at one
     and four waves per SIMD, alone and with independent vector FMAs between the
     MFMAs, plus the vector FMAs alone.  The value is the random-operand FP4
@@ -755,6 +756,13 @@ def bench_mfma_ceiling(args, torch):
                 assert lib.wush_ceiling_fp4(w, cus, it4, b.data_ptr(), out.data_ptr(), sp) == 0
             t = timed(run)
             res[f"fp4_{name}_{label}_TFLOPs"] = round(cus * 4 * it4 * nacc * per_instr / t / 1e12, 1)
+    # operands that change every MFMA, in the matmul's order (64 MFMAs per iteration)
+    it_vary = it4 // 8
+
+    def run_vary():
+        assert lib.wush_ceiling_fp4(2, cus, it_vary, rand_bits.data_ptr(), out.data_ptr(), sp) == 0
+    t = timed(run_vary)
+    res["fp4_16x16x128_random_varying_TFLOPs"] = round(cus * 4 * it_vary * 64 * 16 * 16 * 128 * 2 / t / 1e12, 1)
     it32 = 4000
     for wps in (1, 4):
         for nchain, nvalu in ((2, 0), (8, 0), (2, 4), (2, 8), (8, 8), (0, 8)):
