@@ -440,20 +440,37 @@ def _loop_bodies(code):
 
 
 def test_transform_loop_waits_cover_one_unit():
-    """The streaming transform kernel keeps kDepth units of loads in flight
-    with each unit's stores between them; its prologue issues matching
-    stores into a zero-size resource so that every load wait in the loop
-    waits for one unit's loads only.  In the compiled MXFP4 plane-order kernel
-    (bf16, merged stores) every vmcnt wait of the main loop must therefore
-    allow the same, largest count; a regression to the prologue-only state
-    shows as smaller counts at the loop's first units."""
+    """The streaming transform kernel keeps kDepth = 4 units of x loads in
+    flight, with each unit's stores between them; its prologue issues matching
+    stores into a zero-size resource so that every load wait in the loop waits
+    for one unit's loads only.  Loads and stores retire through one in-order
+    counter, and `s_waitcnt vmcnt(n)` leaves the n most recent operations in
+    flight.  Replaying the compiled loop of the MXFP4 plane-order kernel (bf16,
+    merged stores) in steady state, every wait must therefore leave the loads
+    of the other three units (2 each) in flight; a regression to the
+    prologue-only state shows as smaller counts at the loop's first units."""
     import re
     code = _kernel_code(_device_asm("transform_quant.hip"), "tq_dense_kernelILi32ELi5ELb1ELb1E")
     loops = [b for b in _loop_bodies(code) if sum(1 for l in b if l.startswith("v_mfma")) >= 64]
     assert len(loops) == 1, len(loops)
-    waits = [int(m.group(1)) for l in loops[0] for m in [re.search(r"vmcnt\((\d+)\)", l)] if m]
-    loads = sum(1 for l in loops[0] if l.startswith("buffer_load"))
-    stores = sum(1 for l in loops[0] if l.startswith("buffer_store"))
-    assert loads == 8 and stores == 8, (loads, stores)
-    # each unit: its two loads, waited with 15 and 14 later operations pending
-    assert sorted(set(waits)) == [14, 15], waits
+    ops = []
+    for l in loops[0]:
+        m = re.search(r"vmcnt\((\d+)\)", l)
+        if m:
+            ops.append(int(m.group(1)))
+        elif l.startswith("buffer_load"):
+            ops.append("L")
+        elif l.startswith("buffer_store"):
+            ops.append("S")
+    assert ops.count("L") == 8 and ops.count("S") == 8, ops
+    waits = [o for o in ops if isinstance(o, int)]
+    assert waits, ops
+    issued, in_flight = [], []
+    for rep in range(3):                     # the first copy only fills the history
+        for o in ops:
+            if isinstance(o, int):
+                if rep:
+                    in_flight.append(issued[-o:].count("L") if o else 0)
+            else:
+                issued.append(o)
+    assert min(in_flight) >= 6, (waits, in_flight)
