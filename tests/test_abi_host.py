@@ -450,9 +450,18 @@ def test_transform_loop_waits_cover_one_unit():
     of the other three units (2 each) in flight; a regression to the
     prologue-only state shows as smaller counts at the loop's first units."""
     import re
-    code = _kernel_code(_device_asm("transform_quant.hip"), "tq_dense_kernelILi32ELi5ELb1ELb1E")
+    asm = _device_asm("transform_quant.hip")
+    for stream in (0, 1):   # default and non-temporal x loads (x larger than the Infinity Cache)
+        code = _kernel_code(asm, "tq_dense_kernelILi32ELi5ELb1ELb1ELb%dE" % stream)
+        _check_loop_waits(code, stream)
+
+
+def _check_loop_waits(code, stream):
+    import re
     loops = [b for b in _loop_bodies(code) if sum(1 for l in b if l.startswith("v_mfma")) >= 64]
     assert len(loops) == 1, len(loops)
+    x_loads = [l for l in loops[0] if l.startswith("buffer_load_dwordx4")]
+    assert x_loads and all(l.rstrip().endswith(" nt") == bool(stream) for l in x_loads), x_loads
     ops = []
     for l in loops[0]:
         m = re.search(r"vmcnt\((\d+)\)", l)
