@@ -217,3 +217,32 @@ def test_fullsize_had256_outlier_activations():
         ref = oh.gemv(x, rp, len(rows))
         ok, worst = gemm_close(host(y)[:, rows], ref)
         assert ok, (B, worst)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "int4"])
+def test_fullsize_streamed_x_each_format(fmt):
+    # x larger than the 256 MB Infinity Cache takes the kernels whose x loads are
+    # non-temporal (fp32 x of 2080 x 32768 = 272.6 MB, an even count of 32-blocks
+    # and a multiple of four 16-blocks, so the merged-store kernels); codes and
+    # scales of sampled tokens bit-exact against the oracle.  The transforms are
+    # seeded random matrices: the kernel takes T as given.
+    bs = W.BLOCK[fmt]
+    n, d_in = 2080, 32768
+    assert n * d_in * 4 > 256 << 20
+    print(f"[fullsize] streamed x {fmt} n={n} d_in={d_in}", flush=True)
+    rng = np.random.default_rng([11, bs])
+    X = rng.standard_normal((n, d_in), dtype=np.float32)
+    X[:, rng.choice(d_in, 32, replace=False)] *= 40
+    T = (rng.standard_normal((d_in // bs, bs, bs)) / np.sqrt(bs)).astype(np.float32)
+    g = None
+    if fmt == "nvfp4":
+        g = quant.nvfp4_tensor_scale(quant.apply_transform(T, X[_sample(n, 256, 5)]))
+    sdt = torch.int16 if fmt == "int4" else torch.uint8
+    xc = torch.empty((n, d_in // 2), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((n, d_in // bs), dtype=sdt, device=DEV)
+    W.wush_transform_quant(fmt, to_dev(X), to_dev(T), xc, xs, g=g or 0.0)
+    torch.cuda.synchronize()
+    tok = _sample(n, 24, 6)
+    rc, rs = quant.transform_quant(fmt, T, X[tok], g=g)
+    assert np.array_equal(scales_np(xs, fmt)[tok], rs)
+    assert np.array_equal(host(xc)[tok], rc)
