@@ -242,6 +242,18 @@ def test_fullsize_streamed_x_each_format(fmt):
     xs = torch.empty((n, d_in // bs), dtype=sdt, device=DEV)
     W.wush_transform_quant(fmt, to_dev(X), to_dev(T), xc, xs, g=g or 0.0)
     torch.cuda.synchronize()
+    if fmt == "mxfp4":
+        # the plane-ordered call (its own streamed kernel): the same codes, and scales equal to the
+        # row-major ones re-laid by the library (both buffers zeroed first: rows past n stay zero)
+        xc2 = torch.empty_like(xc)
+        pa = torch.zeros(W.wush_mxfp4_planes_bytes(n, d_in), dtype=torch.uint8, device=DEV)
+        pb = torch.zeros_like(pa)
+        W.wush_transform_quant_mx_planes(to_dev(X), to_dev(T), xc2, pa)
+        W.wush_mxfp4_scale_planes(xs, pb, d_in)
+        torch.cuda.synchronize()
+        assert torch.equal(xc2, xc)
+        assert torch.equal(pa, pb)
+        del xc2, pa, pb
     tok = _sample(n, 24, 6)
     rc, rs = quant.transform_quant(fmt, T, X[tok], g=g)
     assert np.array_equal(scales_np(xs, fmt)[tok], rs)
