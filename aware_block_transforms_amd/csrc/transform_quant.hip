@@ -420,22 +420,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void* base, co
   return buf_rsrc(static_cast<const uint8_t*>(base) + un.row0 * row_bytes, un.rows * row_bytes);
 }
 
-// Raw x of one span of a unit: the lane's 16 (fp32: 32) bytes at offset xoff
-// of the unit's rows (its token's elements col .. col + 7).  STREAM marks the
-// loads non-temporal (cache policy nt).
-template <bool BF16, bool STREAM = false>
-__device__ __forceinline__ void load_x(const void* X, const Unit& un, uint32_t row_bytes, uint32_t xoff,
-                                       uint32_t (&raw)[XRaw<BF16>::kDwords]) {
-  constexpr int kPolicy = STREAM ? 2 : 0;
-  const __amdgpu_buffer_rsrc_t r = unit_rsrc(X, un, row_bytes);
-  const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, xoff, 0, kPolicy));
-  raw[0] = v.x; raw[1] = v.y; raw[2] = v.z; raw[3] = v.w;
-  if constexpr (!BF16) {
-    const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, xoff + 16, 0, kPolicy));
-    raw[4] = w.x; raw[5] = w.y; raw[6] = w.z; raw[7] = w.w;
-  }
-}
-
 // Stores through a unit's resource: lane offset v plus wave-uniform offset s.
 __device__ __forceinline__ void st_b8(uint32_t x, __amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
   __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(x), r, v, s, 0);
@@ -797,34 +781,82 @@ __device__ __forceinline__ void unit_out(const float (&ta)[kSpans][2][8], const 
   }
 }
 
+// Workgroup barrier for the x staging buffers: this wave's LDS traffic done,
+// then s_barrier.  No wait on the vector-memory counter, so the loads of the
+// units ahead stay in flight across it.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte piece of x for the staging buffer: offset v within the unit's rows.
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_piece(const void* X, const Unit& un, uint32_t row_bytes, uint32_t v) {
+  constexpr int kPolicy = STREAM ? 2 : 0;
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(unit_rsrc(X, un, row_bytes), v, 0, kPolicy));
+}
+
 // (X and T are not declared __restrict__: restrict-qualified loads would be
 // moved freely across the scheduling fences.)
+//
+// x loads: the four waves of a workgroup cover 16 tokens x 512 contiguous
+// bytes of x per unit (fp32: 1 KB), so each load instruction reads whole
+// 128-byte lines of two rows (fp32: one row), 512 bytes of each; a wave puts
+// its pieces into an LDS staging buffer (two buffers, one per unit parity,
+// 16-byte chunks XOR-swizzled by row) and, after one workgroup barrier per
+// unit, reads the pieces its lanes compute on: lane (q, j) the 16 bytes (fp32:
+// 32) of token j at span_col, exactly what it would load itself.  A wave whose
+// spans all lie past d_in still loads and stages its share and meets every
+// barrier; its stores go to a unit of no rows.
 template <int BS, int FMT, bool BF16, bool PAIR, bool STREAM>
 __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
     const void* X, const float* T, int n, int d_in, float g, uint8_t* __restrict__ codes, void* __restrict__ scales,
     uint32_t* __restrict__ amax_out, const int* __restrict__ tmap, int ngroups, int upw) {
   constexpr int R = XRaw<BF16>::kDwords;
+  constexpr uint32_t kEsz = BF16 ? 2u : 4u;
+  constexpr int kLd = R / 2;                                     // 1 KB load instructions per wave and unit
+  constexpr int kRowBytes = kWavesPerGroup * kSpans * 32 * kEsz; // the workgroup's bytes of one row
+  constexpr int kRowsPerLd = 1024 / kRowBytes;
+  constexpr int kLanesPerRow = kWave / kRowsPerLd;
+  __shared__ __attribute__((aligned(16))) uint8_t xstage[2][16 * kRowBytes];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, q = lane >> 4;
   const int nblk = d_in / BS;
   const int nspans = (d_in + 31) / 32;
   const int sp0 = (blockIdx.x * kWavesPerGroup + wave) * kSpans;
-  if (sp0 >= nspans) return;                      // wave-uniform; no barrier follows
-  const int u0 = blockIdx.y * upw;                // first unit (16 tokens) of this wave
-  // the lane's byte offset within a unit's rows, per span (fixed for the run)
-  constexpr uint32_t kEsz = BF16 ? 2u : 4u;
+  const bool active = sp0 < nspans;               // wave-uniform
+  const int u0 = blockIdx.y * upw;                // first unit (16 tokens) of this workgroup
   const uint32_t row_bytes = static_cast<uint32_t>(d_in) * kEsz;
-  uint32_t xoff[kSpans];
+  // the lane's loads (offset within the unit's rows) and their staging slots
+  uint32_t xoff[kLd], soff[kLd];
 #pragma unroll
-  for (int s = 0; s < kSpans; ++s) xoff[s] = static_cast<uint32_t>(j * d_in + span_col<BS>(sp0 + s, q, nblk)) * kEsz;
+  for (int i = 0; i < kLd; ++i) {
+    const int row = (wave * kLd + i) * kRowsPerLd + lane / kLanesPerRow, ch = lane % kLanesPerRow;
+    xoff[i] = static_cast<uint32_t>(row) * row_bytes + blockIdx.x * static_cast<uint32_t>(kRowBytes) + ch * 16u;
+    soff[i] = static_cast<uint32_t>(row * kRowBytes + ((ch ^ (row & 7)) * 16));
+  }
+  // the lane's reads: token j's pieces at span_col of each span (a clamped
+  // span reads the last block, which lies in this workgroup's segment)
+  uint32_t roff[kSpans][R / 4];
+#pragma unroll
+  for (int s = 0; s < kSpans; ++s) {
+    const int col = active ? span_col<BS>(sp0 + s, q, nblk) - static_cast<int>(blockIdx.x) * (kRowBytes / static_cast<int>(kEsz)) : 0;
+#pragma unroll
+    for (int h = 0; h < R / 4; ++h) {
+      const int ch = col * static_cast<int>(kEsz) / 16 + h;
+      roff[s][h] = static_cast<uint32_t>(j * kRowBytes + ((ch ^ (j & 7)) * 16));
+    }
+  }
   // T's loads first, then the first units of x; the wait for T (from L2)
   // then leaves the loads of x (from HBM) in flight
   TRaw traw[kSpans];
 #pragma unroll
   for (int s = 0; s < kSpans; ++s) load_t<BS>(T, tmap, ngroups, sp0 + s, nblk, q, j, traw[s]);
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t raw[kDepth][kSpans][R];
+  uint4 ld[kDepth][kLd];
   // Loads and stores retire through one in-order counter, and the loop's
   // waits are shared by all its iterations: each unit's loads are followed by
   // the previous unit's stores in the loop, so here each unit's loads are
@@ -837,7 +869,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
   for (int d = 0; d < kDepth; ++d) {
     const Unit un = unit_at(u0 + d, n);
 #pragma unroll
-    for (int s = 0; s < kSpans; ++s) load_x<BF16, STREAM>(X, un, row_bytes, xoff[s], raw[d][s]);
+    for (int i = 0; i < kLd; ++i) ld[d][i] = load_piece<STREAM>(X, un, row_bytes, xoff[i]);
     if constexpr (kMatchEntry) {
 #pragma unroll
       for (int k = 0; k < stores_per_unit<BS, FMT, PAIR>(); ++k) st_b32(0u, nowhere, 256u * (kDepth * d + k), 0u);
@@ -849,6 +881,25 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
 #pragma unroll
   for (int s = 0; s < kSpans; ++s) t_steps<BS>(traw[s], ta[s]);
   uint32_t run_max = 0;
+  // unit d's pieces through staging buffer d % 2 into the lane's x operands
+  auto exchange = [&](int d, float (&xv)[kSpans][8]) {
+    uint8_t* const st = xstage[d & 1];
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) *reinterpret_cast<uint4*>(st + soff[i]) = ld[d][i];
+    stage_barrier();
+#pragma unroll
+    for (int s = 0; s < kSpans; ++s) {
+      uint32_t xr[R];
+#pragma unroll
+      for (int h = 0; h < R / 4; ++h) {
+        const uint4 v = *reinterpret_cast<const uint4*>(st + roff[s][h]);
+        xr[4 * h] = v.x; xr[4 * h + 1] = v.y; xr[4 * h + 2] = v.z; xr[4 * h + 3] = v.w;
+      }
+      x_steps<BF16>(xr, xv[s]);
+    }
+  };
+  // the unit a wave stores to: its own, or none for a wave past d_in
+  auto out_unit = [&](int unit) { return active ? unit_at(unit, n) : Unit{0, 0u}; };
   // Units u0 .. u0 + upw - 1 (upw a multiple of kDepth), the last kDepth of
   // them without refills.
   int u = 0;
@@ -857,28 +908,26 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       float xv[kSpans][8];
-#pragma unroll
-      for (int s = 0; s < kSpans; ++s) x_steps<BF16>(raw[d][s], xv[s]);
+      exchange(d, xv);
       __builtin_amdgcn_sched_barrier(0);
       const Unit nx = unit_at(u0 + u + d + kDepth, n);
 #pragma unroll
-      for (int s = 0; s < kSpans; ++s) load_x<BF16, STREAM>(X, nx, row_bytes, xoff[s], raw[d][s]);
+      for (int i = 0; i < kLd; ++i) ld[d][i] = load_piece<STREAM>(X, nx, row_bytes, xoff[i]);
       __builtin_amdgcn_sched_barrier(0);
-      unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, j, unit_at(u0 + u + d, n), d_in, g, codes, scales, run_max);
+      unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, j, out_unit(u0 + u + d), d_in, g, codes, scales, run_max);
     }
   }
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
     float xv[kSpans][8];
-#pragma unroll
-    for (int s = 0; s < kSpans; ++s) x_steps<BF16>(raw[d][s], xv[s]);
-    unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, j, unit_at(u0 + u + d, n), d_in, g, codes, scales, run_max);
+    exchange(d, xv);
+    unit_out<BS, FMT, PAIR>(ta, xv, sp0, nblk, q, j, out_unit(u0 + u + d), d_in, g, codes, scales, run_max);
   }
   if constexpr (FMT == kAmax) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
       run_max = max(run_max, static_cast<uint32_t>(__shfl_xor(static_cast<int>(run_max), off)));
-    if (lane == 0) atomicMax(amax_out, run_max);
+    if (lane == 0 && active) atomicMax(amax_out, run_max);
   }
 }
 
