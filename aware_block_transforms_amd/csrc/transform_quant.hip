@@ -13,8 +13,9 @@
 //    tensor maximum.  The transform runs on the fp32 matrix cores as a chain of
 //    v_mfma_f32_16x16x4_f32, which reproduces the pinned FMA chain bit for bit;
 //    each wave streams 16-token units of two adjacent 32-channel spans with the
-//    next units' loads in flight, transposes x across its lane groups with lane
-//    swaps (no LDS), and encodes with the pinned block quantizers.
+//    next units' loads in flight (the workgroup's waves load whole lines
+//    together and exchange them through LDS), transposes x across its lane
+//    groups with lane swaps, and encodes with the pinned block quantizers.
 //  * tq_ident_kernel: the identity transform (a bit-exact copy), one block per
 //    lane.
 //  * tq_hd_kernel: the Hadamard-diagonal variant, one product and log2(bs)
@@ -313,12 +314,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves
 // units with the loads of the next kDepth units in flight.  Lane
 // (g = l / 16, j = l % 16) works on token j of the unit.
 //
-// x: lane (q, j) loads 16 bytes of its token's span, elements 8q .. 8q+7
-// (fp32: 32 bytes, two loads).  At step c the MFMA wants element 4c + g in
+// x: lane (q, j) takes 16 bytes of its token's span, elements 8q .. 8q+7
+// (fp32: 32 bytes), from the workgroup's staging buffer (see the kernel).
+// At step c the MFMA wants element 4c + g in
 // lane group g.  After one v_perm per dword (bf16; it pairs elements 8q + r
 // and 8q + 4 + r), group q holds in dword r what group r needs for steps 2q
 // and 2q+1: a 4 x 4 transpose of dwords across the lane groups, two
-// v_permlane32_swap and two v_permlane16_swap, no LDS round trip.
+// v_permlane32_swap and two v_permlane16_swap.
 //
 // T: at bs 32 the A operand row i of accumulator h is T row
 // 8 (i / 4) + 4 h + i % 4.  Lane group g then ends with outputs 8g .. 8g+7 of
