@@ -641,6 +641,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_persist(const uint8_t* __re
   __builtin_amdgcn_sched_barrier(0);
 
   int par = 0;                                // LDS buffer of the current block
+  // Staging offsets (codes, scale planes) of the blocks iteration k reloads:
+  // block k + 2 of B and k + 3 of A, of this tile or, past its end, of the
+  // next one.  Kept as running offsets, one add and one select each per
+  // iteration: they continue across a tile switch, since the next tile's
+  // block j follows its block j - 1 at +128 bytes whichever tile loaded it.
+  uint32_t dso_b = cur.b + 2 * 128u, sso_b = cur.sb + 2 * kScaleOp;
+  uint32_t dso_a = cur.a + 3 * 128u, sso_a = cur.sa + 3 * kScaleOp;
 #pragma unroll 1
   for (;;) {
     int k = 0;
@@ -648,14 +655,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp4_persist(const uint8_t* __re
     do {
       uint8_t* const cb = par ? buf1 : buf0;
       uint8_t* const nb_ = par ? buf0 : buf1;
-      // blocks k + 2 (B) and k + 3 (A) of this tile, or of the next one past the end
-      const int jb = k + 2, ja = k + 3;
-      const uint32_t dso_b = jb < nb ? cur.b + jb * 128u : nxt.b + (jb - nb) * 128u;
-      const uint32_t sso_b = jb < nb ? cur.sb + jb * kScaleOp : nxt.sb + (jb - nb) * kScaleOp;
-      const uint32_t dso_a = ja < nb ? cur.a + ja * 128u : nxt.a + (ja - nb) * 128u;
-      const uint32_t sso_a = ja < nb ? cur.sa + ja * kScaleOp : nxt.sa + (ja - nb) * kScaleOp;
       phase<true>(c, cb, 1, nb_, 1, dso_b, sso_b, f0, f1, sb, acc);
       phase<false>(c, nb_, 0, cb, 0, dso_a, sso_a, f1, f0, sa, acc);
+      // blocks k + 3 (B) and k + 4 (A) for the next iteration
+      dso_b = k + 3 == nb ? nxt.b : dso_b + 128u;
+      sso_b = k + 3 == nb ? nxt.sb : sso_b + kScaleOp;
+      dso_a = k + 4 == nb ? nxt.a : dso_a + 128u;
+      sso_a = k + 4 == nb ? nxt.sa : sso_a + kScaleOp;
       par ^= 1;
       ++k;
     } while (k < nb);
