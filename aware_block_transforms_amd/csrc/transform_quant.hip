@@ -1065,13 +1065,15 @@ IdentFn select_ident(int fmt, int bs, bool bf16) {
   return nullptr;
 }
 
-// Units (16 tokens) per wave of the dense kernel: about eight waves per SIMD
-// over the whole grid, at least kDepth units each, a multiple of kDepth.
+// Units (16 tokens) per wave of the dense kernel: about sixteen waves per
+// SIMD over the whole grid (four resident at a time, so several rounds, and
+// short runs that keep the last round's imbalance small), at least kDepth
+// units each, a multiple of kDepth.
 int dense_units_per_wave(int n, int d_in) {
   const long units = (n + 15) / 16;
   const long span_groups = ((d_in + 31) / 32 + kSpans - 1) / kSpans;
   const long wave_cols = (span_groups + kWavesPerGroup - 1) / kWavesPerGroup * kWavesPerGroup;
-  const long target_waves = 8L * 4 * 256;     // 8 waves on each of the 1024 SIMDs
+  const long target_waves = 16L * 4 * 256;    // 16 waves on each of the 1024 SIMDs
   const long slices = std::max(1L, target_waves / wave_cols);
   long upw = (units + slices - 1) / slices;
   upw = (upw + kDepth - 1) / kDepth * kDepth;
