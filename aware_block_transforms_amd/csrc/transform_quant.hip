@@ -14,8 +14,8 @@
 //    v_mfma_f32_16x16x4_f32, which reproduces the pinned FMA chain bit for bit;
 //    each wave streams 16-token units of two adjacent 32-channel spans with the
 //    next units' loads in flight (the workgroup's waves load whole lines
-//    together and exchange them through LDS), transposes x across its lane
-//    groups with lane swaps, and encodes with the pinned block quantizers.
+//    together and exchange them through LDS, from where each lane reads x in
+//    the MFMA's step order), and encodes with the pinned block quantizers.
 //  * tq_ident_kernel: the identity transform (a bit-exact copy), one block per
 //    lane.
 //  * tq_hd_kernel: the Hadamard-diagonal variant, one product and log2(bs)
@@ -314,13 +314,15 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) __attribute__((amdgpu_waves
 // units with the loads of the next kDepth units in flight.  Lane
 // (g = l / 16, j = l % 16) works on token j of the unit.
 //
-// x: lane (q, j) takes 16 bytes of its token's span, elements 8q .. 8q+7
-// (fp32: 32 bytes), from the workgroup's staging buffer (see the kernel).
-// At step c the MFMA wants element 4c + g in
-// lane group g.  After one v_perm per dword (bf16; it pairs elements 8q + r
-// and 8q + 4 + r), group q holds in dword r what group r needs for steps 2q
-// and 2q+1: a 4 x 4 transpose of dwords across the lane groups, two
-// v_permlane32_swap and two v_permlane16_swap.
+// x: at step c the MFMA wants element 4c + g of the lane's token in lane
+// group g, and the lane reads it from the workgroup's staging buffer (see the
+// kernel).  bf16: elements 4c + g for c = 0 .. 7 are the low (g even) or high
+// (g odd) halves of every other dword of the span, two in each 16-byte piece,
+// so a lane reads them with one two-dword LDS read per piece and widens each
+// with one v_perm (its two bytes on top, zeros below): no lane exchange.
+// fp32: lane (q, j) reads elements 8q .. 8q+7 (32 bytes), and a 4 x 4
+// transpose of dwords across the lane groups (two v_permlane32_swap and two
+// v_permlane16_swap per four dwords) gives group g what it needs.
 //
 // T: at bs 32 the A operand row i of accumulator h is T row
 // 8 (i / 4) + 4 h + i % 4.  Lane group g then ends with outputs 8g .. 8g+7 of
@@ -470,29 +472,16 @@ __device__ __forceinline__ void store_plane_scale(void* scales, const Unit& un, 
   st_b8(sc, buf_rsrc(base, 2048u), static_cast<uint32_t>(j) < un.rows ? off : 0x80000000u, 0u);
 }
 
-// x operands of the eight MFMA steps of one span for lane (g, j).
-template <bool BF16>
-__device__ __forceinline__ void x_steps(const uint32_t (&raw)[XRaw<BF16>::kDwords], float (&xv)[8]) {
-  if constexpr (BF16) {
-    uint32_t d[4];
+// x operands of the eight MFMA steps of one span for lane (g, j), from the
+// lane's 32 bytes of fp32 x (elements 8g .. 8g+7 of its token).
+__device__ __forceinline__ void x_steps_f32(const uint32_t (&raw)[8], float (&xv)[8]) {
+  uint32_t lo[4] = {raw[0], raw[1], raw[2], raw[3]}, hi[4] = {raw[4], raw[5], raw[6], raw[7]};
+  transpose4(lo);
+  transpose4(hi);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      d[r] = __builtin_amdgcn_perm(raw[2 + (r >> 1)], raw[r >> 1], (r & 1) ? 0x07060302u : 0x05040100u);
-    transpose4(d);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      xv[2 * q] = __uint_as_float(d[q] << 16);
-      xv[2 * q + 1] = __uint_as_float(d[q] & 0xffff0000u);
-    }
-  } else {
-    uint32_t lo[4] = {raw[0], raw[1], raw[2], raw[3]}, hi[4] = {raw[4], raw[5], raw[6], raw[7]};
-    transpose4(lo);
-    transpose4(hi);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      xv[2 * q] = __uint_as_float(lo[q]);
-      xv[2 * q + 1] = __uint_as_float(hi[q]);
-    }
+  for (int q = 0; q < 4; ++q) {
+    xv[2 * q] = __uint_as_float(lo[q]);
+    xv[2 * q + 1] = __uint_as_float(hi[q]);
   }
 }
 
@@ -807,9 +796,11 @@ __device__ __forceinline__ uint4 load_piece(const void* X, const Unit& un, uint3
 // bytes of x per unit (fp32: 1 KB), so each load instruction reads whole
 // 128-byte lines of two rows (fp32: one row), 512 bytes of each; a wave puts
 // its pieces into an LDS staging buffer (two buffers, one per unit parity,
-// 16-byte chunks XOR-swizzled by row) and, after one workgroup barrier per
-// unit, reads the pieces its lanes compute on: lane (q, j) the 16 bytes (fp32:
-// 32) of token j at span_col, exactly what it would load itself.  A wave whose
+// 16-byte chunks XOR-swizzled by row & 15, so that the 16 tokens of a read
+// fall in 16 different chunks) and, after one workgroup barrier per unit,
+// reads what its lanes compute on: bf16 lane (g, j) the dwords of token j
+// holding elements 4c + g, fp32 lane (q, j) the 32 bytes of token j at
+// span_col.  A wave whose
 // spans all lie past d_in still loads and stages its share and meets every
 // barrier; its stores go to a unit of no rows.
 template <int BS, int FMT, bool BF16, bool PAIR, bool STREAM>
@@ -838,20 +829,34 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
   for (int i = 0; i < kLd; ++i) {
     const int row = (wave * kLd + i) * kRowsPerLd + lane / kLanesPerRow, ch = lane % kLanesPerRow;
     xoff[i] = static_cast<uint32_t>(row) * row_bytes + blockIdx.x * static_cast<uint32_t>(kRowBytes) + ch * 16u;
-    soff[i] = static_cast<uint32_t>(row * kRowBytes + ((ch ^ (row & 7)) * 16));
+    soff[i] = static_cast<uint32_t>(row * kRowBytes + ((ch ^ (row & 15)) * 16));
   }
   // the lane's reads: token j's pieces at span_col of each span (a clamped
   // span reads the last block, which lies in this workgroup's segment)
-  uint32_t roff[kSpans][R / 4];
+  constexpr int kReads = BF16 ? 4 : R / 4;
+  uint32_t roff[kSpans][kReads];
 #pragma unroll
   for (int s = 0; s < kSpans; ++s) {
-    const int col = active ? span_col<BS>(sp0 + s, q, nblk) - static_cast<int>(blockIdx.x) * (kRowBytes / static_cast<int>(kEsz)) : 0;
+    if constexpr (BF16) {
+      // bf16: lane group q takes elements 4c + q of its token (c = 0 .. 7),
+      // the low (q even) or high (q odd) half of every other dword: two per
+      // 16-byte piece h, which holds elements 8h .. 8h + 7 of the span
 #pragma unroll
-    for (int h = 0; h < R / 4; ++h) {
-      const int ch = col * static_cast<int>(kEsz) / 16 + h;
-      roff[s][h] = static_cast<uint32_t>(j * kRowBytes + ((ch ^ (j & 7)) * 16));
+      for (int h = 0; h < 4; ++h) {
+        const int col = active ? span_col<BS>(sp0 + s, h, nblk) - static_cast<int>(blockIdx.x) * (kRowBytes / 2) : 0;
+        roff[s][h] = static_cast<uint32_t>(j * kRowBytes + (((col / 8) ^ (j & 15)) * 16) + (q >> 1) * 4);
+      }
+    } else {
+      const int col = active ? span_col<BS>(sp0 + s, q, nblk) - static_cast<int>(blockIdx.x) * (kRowBytes / static_cast<int>(kEsz)) : 0;
+#pragma unroll
+      for (int h = 0; h < R / 4; ++h) {
+        const int ch = col * static_cast<int>(kEsz) / 16 + h;
+        roff[s][h] = static_cast<uint32_t>(j * kRowBytes + ((ch ^ (j & 15)) * 16));
+      }
     }
   }
+  // bf16 -> fp32 of the half a lane group takes: its two bytes on top, zeros below
+  const uint32_t xsel = (q & 1) ? 0x03020c0cu : 0x01000c0cu;
   // T's loads first, then the first units of x; the wait for T (from L2)
   // then leaves the loads of x (from HBM) in flight
   TRaw traw[kSpans];
@@ -891,13 +896,22 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void tq_dense_kernel(
     stage_barrier();
 #pragma unroll
     for (int s = 0; s < kSpans; ++s) {
-      uint32_t xr[R];
+      if constexpr (BF16) {
 #pragma unroll
-      for (int h = 0; h < R / 4; ++h) {
-        const uint4 v = *reinterpret_cast<const uint4*>(st + roff[s][h]);
-        xr[4 * h] = v.x; xr[4 * h + 1] = v.y; xr[4 * h + 2] = v.z; xr[4 * h + 3] = v.w;
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t* p = reinterpret_cast<const uint32_t*>(st + roff[s][h]);
+          xv[s][2 * h] = __uint_as_float(__builtin_amdgcn_perm(p[0], p[0], xsel));
+          xv[s][2 * h + 1] = __uint_as_float(__builtin_amdgcn_perm(p[2], p[2], xsel));
+        }
+      } else {
+        uint32_t xr[R];
+#pragma unroll
+        for (int h = 0; h < R / 4; ++h) {
+          const uint4 v = *reinterpret_cast<const uint4*>(st + roff[s][h]);
+          xr[4 * h] = v.x; xr[4 * h + 1] = v.y; xr[4 * h + 2] = v.z; xr[4 * h + 3] = v.w;
+        }
+        x_steps_f32(xr, xv[s]);
       }
-      x_steps<BF16>(xr, xv[s]);
     }
   };
   // the unit a wave stores to: its own, or none for a wave past d_in
